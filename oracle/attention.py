@@ -1,0 +1,98 @@
+"""Exact block-sparse softmax attention (oracle), fp64.
+
+Every page treats full 3D attention (every token against every token, quadratic
+cost) as the thing being replaced: Radial Attention explainer (aibr.jp/archives/
+112136) sec. 1, Sliding Tile Attention explainer (aibr.jp/archives/60739) sec. 1,
+NABLA explainer (aibr.jp/archives/124678) sec. 1; the sparse methods compute the
+same attention over the kept blocks only (SPADE summary, gist.science/ja/paper/
+2608.03335, "The solution", part 3: head-wise sparse attention).  Reading taken:
+for a query token of query block i, the keys are all valid tokens of the kept key
+blocks J_i, and
+
+    s_j = q . k_j * scale,  m = max_j s_j,  p_j = exp(s_j - m),  l = sum_j p_j,
+    o = sum_j p_j v_j / l,  lse = m + ln l.
+
+A row with no kept block has o = 0 and lse = -inf.
+"""
+import numpy as np
+
+
+def block_softmax(qi, kj, scale):
+    """Softmax probabilities of a query block over a key set: [nq, nk] fp64."""
+    s = (qi @ kj.T) * scale
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    return p / p.sum(axis=1, keepdims=True)
+
+
+def _slab(n_slabs, b, h, heads):
+    return 0 if n_slabs == 1 else b * heads + h
+
+
+def _key_tokens(cols, block_k, nk):
+    """Ascending token indices of the kept key blocks."""
+    if len(cols) == 0:
+        return np.zeros(0, dtype=np.int64)
+    return np.concatenate([np.arange(j * block_k, min((j + 1) * block_k, nk)) for j in cols])
+
+
+def attention(q, k, v, row_ptr, col_idx, block_q, block_k, scale, n_slabs=1):
+    """q [B, Nq, Hh, D], k/v [B, Nk, Hh, D] -> (o [B, Nq, Hh, D] fp64, lse [B, Hh, Nq] fp64).
+
+    CSR row r = slab * n_qblocks + qblock, slab = 0 when n_slabs == 1, else b*Hh + h."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, nq, Hh, D = q.shape
+    nk = k.shape[1]
+    nbq = -(-nq // block_q)
+    o = np.zeros((B, nq, Hh, D))
+    lse = np.full((B, Hh, nq), -np.inf)
+    for b in range(B):
+        for h in range(Hh):
+            base = _slab(n_slabs, b, h, Hh) * nbq
+            for i in range(nbq):
+                r = base + i
+                toks = _key_tokens(col_idx[row_ptr[r]:row_ptr[r + 1]], block_k, nk)
+                q0, q1 = i * block_q, min((i + 1) * block_q, nq)
+                if len(toks) == 0:
+                    continue
+                s = (q[b, q0:q1, h] @ k[b, toks, h].T) * scale
+                m = s.max(axis=1, keepdims=True)
+                p = np.exp(s - m)
+                l = p.sum(axis=1, keepdims=True)
+                o[b, q0:q1, h] = (p @ v[b, toks, h]) / l
+                lse[b, h, q0:q1] = (m + np.log(l))[:, 0]
+    return o, lse
+
+
+def attention_rows(q_rows, row_tokens, kh, vh, row_ptr, col_idx, row_base,
+                   block_q, block_k, scale, chunk=32):
+    """Selected output rows of one (batch, head), by the masked-dense definition.
+
+    q_rows [R, D] are the query vectors of query tokens `row_tokens`; kh, vh [Nk, D]
+    the head's keys and values; the CSR row of token t is row_base + t // block_q.
+    Scores of keys outside the kept blocks are set to -inf, then an ordinary
+    softmax over all Nk keys is taken.  Returns (o [R, D], lse [R])."""
+    q_rows = np.asarray(q_rows, np.float64)
+    nk = kh.shape[0]
+    out = np.zeros_like(q_rows)
+    lse = np.full(len(q_rows), -np.inf)
+    for c0 in range(0, len(q_rows), chunk):
+        c1 = min(len(q_rows), c0 + chunk)
+        s = (q_rows[c0:c1] @ kh.T) * scale
+        allowed = np.zeros((c1 - c0, nk), dtype=bool)
+        for a, t in enumerate(row_tokens[c0:c1]):
+            r = row_base + int(t) // block_q
+            for j in col_idx[row_ptr[r]:row_ptr[r + 1]]:
+                allowed[a, j * block_k:min((j + 1) * block_k, nk)] = True
+        s = np.where(allowed, s, -np.inf)
+        m = s.max(axis=1, keepdims=True)
+        ok = np.isfinite(m[:, 0])
+        m = np.where(np.isfinite(m), m, 0.0)
+        p = np.exp(s - m)
+        l = p.sum(axis=1, keepdims=True)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            out[c0:c1] = np.where(ok[:, None], (p @ vh) / l, 0.0)
+            lse[c0:c1] = np.where(ok, (m + np.log(l))[:, 0], -np.inf)
+    return out, lse
