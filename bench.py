@@ -1,0 +1,237 @@
+"""Benchmark of the block-sparse 3D-video attention path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input, all on
+the GPU with the inputs resident in HBM:
+    tile reorder of Q, K, V -> STA mask -> block-sparse attention -> inverse
+    reorder of O
+on the STA workload (24 heads, head_dim 128, bf16, 30x48x80 = 115,200 tokens,
+6x8x8 tiles = 384-token blocks on a 5x6x10 tile grid, 3x3x5 tile window clipped
+at the border).
+
+value       = kept-block attention FLOPs (4 * D * sum of nq*nk over kept block
+              pairs, true token counts) / wall time of a step, TFLOP/s.
+roofline    = the attention kernel alone: the same FLOPs / its mean launch time
+              measured with HIP events on its stream, against the bf16 dense
+              MFMA peak (2.5 PFLOP/s).
+speedup     = the same kernel on an all-ones mask (dense attention) / sparse.
+cpu_baseline= the fp64 oracle on a bounded sample (the same path for a subset of
+              heads), FLOPs counted the same way.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-dense] [--no-cpu]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+METRIC = "block-sparse attn effective TFLOPS (kept blocks), % bf16 MFMA peak; speedup vs dense"
+WORKLOAD = "sta"
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_masks_amd", "csrc", "attn_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_sta_traffic.json")
+
+
+def attn_flops(rp, ci, block_q, block_k, nq, nk, D, bh, n_slabs):
+    """4*D*sum over kept (i, j) of nq(i)*nk(j) with true (ragged) token counts, over
+    all bh = batch*heads (a shared mask, n_slabs = 1, counts once per (b, h))."""
+    rp = np.asarray(rp, dtype=np.int64)
+    ci = np.asarray(ci, dtype=np.int64)
+    nbq = -(-nq // block_q)
+    qsz = np.minimum(block_q, nq - np.arange(nbq) * block_q)
+    ksz = np.minimum(block_k, nk - ci * block_k)
+    csum = np.concatenate([[0], np.cumsum(ksz)])
+    per_row = csum[rp[1:]] - csum[rp[:-1]]            # kept key tokens per CSR row
+    total = float((per_row * np.tile(qsz, n_slabs)).sum())
+    return 4.0 * D * total * (bh if n_slabs == 1 else 1)
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def cpu_baseline(x, cfg, target_s=12.0):
+    """The fp64 oracle on a bounded sample: the same path (reorder, STA mask,
+    attention, inverse reorder) for whole heads, taken in order until about
+    target_s seconds of CPU work have run."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    grid, tile, window = cfg["grid"], cfg["tile"], cfg["window"]
+    D = cfg["head_dim"]
+    bq = tile[0] * tile[1] * tile[2]
+    N = x["q"].shape[1]
+    t0 = time.perf_counter()
+    rp, ci = oracle.mask_sta(grid, tile, window)
+    flops, heads_done = 0.0, 0
+    for h in range(cfg["heads"]):
+        qh, kh, vh = (x[w][:, :, h:h + 1].double().numpy() for w in ("q", "k", "v"))
+        qt, kt, vt = (oracle.tile_reorder(a, grid, tile) for a in (qh, kh, vh))
+        o, _ = oracle.attention(qt, kt, vt, rp, ci, bq, bq, D ** -0.5, 1)
+        oracle.tile_reorder(o, grid, tile, inverse=True)
+        flops += attn_flops(rp, ci, bq, bq, N, N, D, 1, 1)
+        heads_done += 1
+        if time.perf_counter() - t0 > target_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 numpy oracle, full path (reorder, STA mask, attention, inverse reorder) for "
+                      f"{heads_done} of {cfg['heads']} heads, {dt:.1f} s wall; host has "
+                      f"{len(os.sched_getaffinity(0))} cores available"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--dense-reps", type=int, default=3)
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the path shards by head "
+              "with no communication and multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import block_sparse_attention_masks_amd as vsa
+    from workloads import gen
+    from workloads.configs import CONFIGS
+
+    cfg = CONFIGS[WORKLOAD]
+    grid, tile, window = cfg["grid"], cfg["tile"], cfg["window"]
+    H, D = cfg["heads"], cfg["head_dim"]
+    block = tile[0] * tile[1] * tile[2]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_gen = time.perf_counter()
+    x = gen.make_inputs(WORKLOAD)
+    print(f"[bench] inputs generated in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    q, k, v = (x[w].to(dev) for w in ("q", "k", "v"))
+    N = q.shape[1]
+    stream = torch.cuda.current_stream(dev)
+    qt, kt, vt, ot = (torch.empty_like(q) for _ in range(4))
+    o = torch.empty_like(q)
+    lse = torch.empty((1, H, N), dtype=torch.float32, device=dev)
+    nbq = N // block
+    cap = vsa.sta_capacity(grid, tile, window)
+    rp = torch.empty(nbq + 1, dtype=torch.int32, device=dev)
+    ci = torch.empty(cap, dtype=torch.int32, device=dev)
+
+    ev = {name: [] for name in ("reorder_qkv", "mask", "attn", "reorder_o")}
+
+    def step(record):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
+        if record:
+            marks[0].record(stream)
+        for src, dst in ((q, qt), (k, kt), (v, vt)):
+            vsa.vsa_tile_reorder(src, grid, tile, out=dst)
+        if record:
+            marks[1].record(stream)
+        vsa.vsa_mask_sta(grid, tile, window, dev, row_ptr=rp, col_idx=ci)
+        if record:
+            marks[2].record(stream)
+        vsa.vsa_block_sparse_attn_fwd(qt, kt, vt, rp, ci, block, block, 1, out=ot, lse=lse)
+        if record:
+            marks[3].record(stream)
+        vsa.vsa_tile_reorder(ot, grid, tile, inverse=True, out=o)
+        if record:
+            marks[4].record(stream)
+        return marks
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    all_marks = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        all_marks.append(step(True))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for m in all_marks:
+        for i, name in enumerate(ev):
+            ev[name].append(m[i].elapsed_time(m[i + 1]))
+    ms_step = wall * 1e3 / args.steps
+
+    rp_h = rp.cpu().numpy()
+    ci_h = ci[: int(rp_h[-1])].cpu().numpy()
+    flops = attn_flops(rp_h, ci_h, block, block, N, N, D, H, 1)
+    attn_ms = float(np.mean(ev["attn"]))
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    print(f"[bench] step {ms_step:.3f} ms; per-kernel ms: " +
+          ", ".join(f"{k_}={np.mean(v_):.3f}" for k_, v_ in ev.items()), file=sys.stderr, flush=True)
+
+    dense = None
+    if not args.no_dense:
+        drp, dci = vsa.all_ones_mask(nbq, nbq, dev)
+        dms = []
+        vsa.vsa_block_sparse_attn_fwd(qt, kt, vt, drp, dci, block, block, 1, out=ot, lse=lse)
+        for _ in range(args.dense_reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            vsa.vsa_block_sparse_attn_fwd(qt, kt, vt, drp, dci, block, block, 1, out=ot, lse=lse)
+            b.record(stream)
+            b.synchronize()
+            dms.append(a.elapsed_time(b))
+        dense_flops = 4.0 * D * N * N * H
+        dense = {"ms": float(np.mean(dms)), "tflops": dense_flops / (np.mean(dms) * 1e-3) / 1e12,
+                 "speedup_vs_dense": float(np.mean(dms)) / attn_ms}
+        print(f"[bench] dense run {dense['ms']:.2f} ms ({dense['tflops']:.1f} TFLOP/s)", file=sys.stderr, flush=True)
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("attn_src_sha256_16") == source_hash(ATTN_SRC):
+            traffic = tr.get("bytes_per_launch")
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(x, cfg)
+        print(f"[bench] cpu baseline {cpu['value']:.4f} TFLOP/s ({cpu['sample']})", file=sys.stderr, flush=True)
+
+    out = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "sta: 1 x 24 heads x 115,200 tokens (30x48x80 grid), head_dim 128, bf16, "
+                               "6x8x8 tiles (384-token blocks), 3x3x5 tile window clipped at the border",
+                   "global_batch": 1, "seq_len": N, "heads": H, "head_dim": D, "block": block,
+                   "kept_block_pairs": int(len(ci_h)), "kept_fraction": round(len(ci_h) / nbq ** 2, 5),
+                   "parallelism": "none (one GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "attn_fwd_bf16_kernel<128>",
+                     "flops_per_launch": flops, "ms_per_launch": round(attn_ms, 4)},
+        "cpu_baseline": cpu,
+        "attn_tflops": round(attn_tflops, 2),
+        "attn_pct_bf16_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
+        "speedup_vs_dense": None if dense is None else round(dense["speedup_vs_dense"], 3),
+        "dense_ms": None if dense is None else round(dense["ms"], 3),
+        "dense_tflops": None if dense is None else round(dense["tflops"], 2),
+        "kernel_ms": {k_: round(float(np.mean(v_)), 4) for k_, v_ in ev.items()},
+        "reorder_gbs": round(4 * 2 * q.numel() * 2 / (np.sum([np.mean(ev["reorder_qkv"]), np.mean(ev["reorder_o"])]) * 1e-3) / 1e9, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,227 @@
+"""ctypes binding of libvsa.so: argument marshalling only.
+
+Torch tensors supply device memory and the stream; every step of the path runs
+in the library's HIP kernels.  There is no CPU fallback: if the library is not
+built, every call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libvsa.so")
+
+VSA_F32, VSA_BF16 = 0, 1
+_DTYPE = {torch.float32: VSA_F32, torch.bfloat16: VSA_BF16}
+
+
+class VsaError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+class Select(ctypes.Structure):
+    _fields_ = [("cdf_threshold", ctypes.c_double), ("topk", ctypes.c_int32),
+                ("n_forced", ctypes.c_int32), ("forced", ctypes.POINTER(ctypes.c_int32))]
+
+
+_lib = None
+
+_P, _I32, _I64, _F32, _F64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double
+_SIGS = {
+    "vsa_status_string": ([_I32], ctypes.c_char_p),
+    "vsa_tile_reorder": ([_P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I64, _I32, _P], _I32),
+    "vsa_mask_sta": ([_I32] * 9 + [_P, _P, _I64, _P], _I32),
+    "vsa_mask_radial": ([_I32, _I32, _I32, _P, _P, _I64, _P], _I32),
+    "vsa_mask_nabla": ([_P, _P, _I32, _I64, _I32, _I32, _I64, _I64, _I32, _I32, _F64,
+                        ctypes.POINTER(Select), _P, _P, _I64, _P, ctypes.POINTER(ctypes.c_size_t), _P], _I32),
+    "vsa_block_sparse_attn_fwd": ([_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I64, _I64, _I32, _I32,
+                                   _P, _P, _I32, _F32, _P, ctypes.POINTER(ctypes.c_size_t), _P], _I32),
+}
+EXPORTS = tuple(_SIGS)
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_sparse_attention_masks_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(h, name)
+            fn.argtypes, fn.restype = args, res
+        _lib = h
+    return _lib
+
+
+def status_string(status):
+    return lib().vsa_status_string(status).decode()
+
+
+def _check(status, where):
+    if status != 0:
+        raise VsaError(status, where)
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _require(t, name, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU (no CPU path exists)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+# ----------------------------------------------------------------------------- calls
+def vsa_tile_reorder(src, grid, tile, inverse=False, out=None):
+    """Tile reorder of src [B, T*H*W, heads, head_dim] (any dtype); returns dst."""
+    _require(src, "src")
+    out = torch.empty_like(src) if out is None else out
+    _require(out, "out", src.device)
+    T, H, W = grid
+    tt, th, tw = tile
+    row_bytes = src[0, 0].numel() * src.element_size()
+    _check(lib().vsa_tile_reorder(_ptr(src), _ptr(out), src.shape[0], T, H, W, tt, th, tw,
+                                  row_bytes, int(bool(inverse)), _stream(src)), "vsa_tile_reorder")
+    return out
+
+
+def sta_capacity(grid, tile, window):
+    n = [g // t for g, t in zip(grid, tile)]
+    return n[0] * n[1] * n[2] * min(window[0], n[0]) * min(window[1], n[1]) * min(window[2], n[2])
+
+
+def vsa_mask_sta(grid, tile, window, device, row_ptr=None, col_idx=None):
+    """STA tile-window mask -> (row_ptr, col_idx) int32 device tensors.
+
+    col_idx is allocated at the capacity the call requires; its first
+    row_ptr[-1] entries are the mask.  Preallocated outputs may be passed."""
+    n = (grid[0] // tile[0]) * (grid[1] // tile[1]) * (grid[2] // tile[2])
+    cap = sta_capacity(grid, tile, window)
+    if row_ptr is None:
+        row_ptr = torch.empty(n + 1, dtype=torch.int32, device=device)
+    if col_idx is None:
+        col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=device)
+    _require(row_ptr, "row_ptr")
+    _require(col_idx, "col_idx", row_ptr.device)
+    if row_ptr.numel() != n + 1 or row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise ValueError("row_ptr must be int32 [n_tiles + 1] and col_idx int32")
+    _check(lib().vsa_mask_sta(*grid, *tile, *window, _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
+                              _stream(row_ptr)), "vsa_mask_sta")
+    return row_ptr, col_idx
+
+
+def vsa_mask_radial(T, S, block, device, row_ptr=None, col_idx=None):
+    """Radial mask over raster order -> (row_ptr, col_idx); col_idx holds
+    n_blocks^2 entries, the first row_ptr[-1] of which are the mask."""
+    nb = -(-(T * S) // block)
+    if row_ptr is None:
+        row_ptr = torch.empty(nb + 1, dtype=torch.int32, device=device)
+    if col_idx is None:
+        col_idx = torch.empty(nb * nb, dtype=torch.int32, device=device)
+    _require(row_ptr, "row_ptr")
+    _require(col_idx, "col_idx", row_ptr.device)
+    if row_ptr.numel() != nb + 1 or row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise ValueError("row_ptr must be int32 [n_blocks + 1] and col_idx int32")
+    _check(lib().vsa_mask_radial(T, S, block, _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
+                                 _stream(row_ptr)), "vsa_mask_radial")
+    return row_ptr, col_idx
+
+
+def _select(threshold, topk, forced):
+    flat = [int(x) for r in forced for x in r]
+    arr = (ctypes.c_int32 * max(1, len(flat)))(*flat)
+    sel = Select(float(threshold if threshold is not None else 1.0), int(topk), len(forced),
+                 ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)))
+    return sel, arr
+
+
+def nabla_workspace_bytes(q, k, block_q, block_k, scale=None, threshold=1.0, topk=0, forced=()):
+    sel, _keep = _select(threshold, topk, forced)
+    nbytes = ctypes.c_size_t(0)
+    B, nq, Hh, D = q.shape
+    rp = ctypes.c_void_p(16)  # never dereferenced by a size query
+    _check(lib().vsa_mask_nabla(_ptr(q), _ptr(k), _DTYPE[q.dtype], B, Hh, D, nq, k.shape[1],
+                                block_q, block_k, float(scale if scale is not None else D ** -0.5),
+                                ctypes.byref(sel), rp, rp, 0, None, ctypes.byref(nbytes), None),
+           "vsa_mask_nabla")
+    return nbytes.value
+
+
+def vsa_mask_nabla(q, k, block_q, block_k, scale=None, threshold=None, topk=0, forced=(),
+                   workspace=None):
+    """NABLA (threshold) or anchor + recent + top-k (topk > 0) mask, one slab per
+    (batch, head) -> (row_ptr, col_idx)."""
+    _require(q, "q")
+    _require(k, "k", q.device)
+    B, nq, Hh, D = q.shape
+    nk = k.shape[1]
+    scale = D ** -0.5 if scale is None else scale
+    sel, _keep = _select(threshold, topk, forced)
+    nbq, nbk = -(-nq // block_q), -(-nk // block_k)
+    rows = B * Hh * nbq
+    row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=q.device)
+    col_idx = torch.empty(rows * nbk, dtype=torch.int32, device=q.device)
+    need = nabla_workspace_bytes(q, k, block_q, block_k, scale, sel.cdf_threshold, topk, forced)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    nbytes = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    _check(lib().vsa_mask_nabla(_ptr(q), _ptr(k), _DTYPE[q.dtype], B, Hh, D, nq, nk, block_q,
+                                block_k, float(scale), ctypes.byref(sel), _ptr(row_ptr),
+                                _ptr(col_idx), rows * nbk, _ptr(workspace), ctypes.byref(nbytes),
+                                _stream(q)), "vsa_mask_nabla")
+    return row_ptr, col_idx
+
+
+def vsa_block_sparse_attn_fwd(q, k, v, row_ptr, col_idx, block_q, block_k, n_slabs=1, scale=None,
+                              out=None, lse=None, want_lse=True):
+    """Exact softmax attention over the kept blocks -> (o, lse or None)."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("row_ptr", row_ptr), ("col_idx", col_idx)):
+        _require(t, name, q.device)
+    B, nq, Hh, D = q.shape
+    nk = k.shape[1]
+    if k.shape != (B, nk, Hh, D) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v shapes / dtypes do not match")
+    if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise ValueError("row_ptr and col_idx must be int32")
+    if row_ptr.numel() != n_slabs * -(-nq // block_q) + 1:
+        raise ValueError("row_ptr length does not match n_slabs * n_qblocks + 1")
+    scale = D ** -0.5 if scale is None else scale
+    out = torch.empty_like(q) if out is None else out
+    _require(out, "out", q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hh, nq), dtype=torch.float32, device=q.device)
+    _check(lib().vsa_block_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                           _DTYPE[q.dtype], B, Hh, D, nq, nk, block_q, block_k,
+                                           _ptr(row_ptr), _ptr(col_idx), n_slabs, float(scale),
+                                           None, None, _stream(q)), "vsa_block_sparse_attn_fwd")
+    return out, lse
+
+
+def all_ones_mask(n_qblocks, n_kblocks, device):
+    """All-ones CSR (dense attention) built on the device with torch fills."""
+    row_ptr = torch.arange(0, (n_qblocks + 1) * n_kblocks, n_kblocks, dtype=torch.int32, device=device)
+    col_idx = torch.arange(n_kblocks, dtype=torch.int32, device=device).repeat(n_qblocks)
+    return row_ptr, col_idx
+
+
+def ar_forced_ranges(frame_tokens, n_frames, anchor_frames, recent_frames, block):
+    """Key-block ranges [lo, hi) of the anchor frames and the most recent frames of a
+    KV cache of n_frames frames (raster, `block`-token blocks)."""
+    nbk = -(-(frame_tokens * n_frames) // block)
+    return [(0, -(-(anchor_frames * frame_tokens) // block)),
+            (((n_frames - recent_frames) * frame_tokens) // block, nbk)]

@@ -1,0 +1,54 @@
+"""Build libvsa.so (the HIP kernels and their C ABI) for gfx950, in-tree.
+
+Usage: python -m block_sparse_attention_masks_amd.build  [-v]
+Every .hip file under csrc/ is compiled by hipcc to an object, in parallel, and
+the objects are linked into block_sparse_attention_masks_amd/libvsa.so.
+"""
+import glob
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+LIB = os.path.join(PKG, "libvsa.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    "-Wno-unused-function", "-Wno-unknown-pragmas",
+    # keep the compiler from emitting packed fp32 arithmetic (v_pk_*_f32)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    # the host pass warns that it does not know the packed-fp32 feature: harmless
+    msgs = [ln for ln in r.stderr.splitlines() if ln.strip() and "packed-fp32-ops" not in ln
+            and "is not a recognized feature for this target" not in ln]
+    if msgs and verbose:
+        print("\n".join(msgs), file=sys.stderr)
+
+
+def build(verbose=False):
+    srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
+    out_dir = os.path.join(PKG, "_build")
+    os.makedirs(out_dir, exist_ok=True)
+    objs = [os.path.join(out_dir, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    with ThreadPoolExecutor(min(8, len(srcs))) as ex:
+        list(ex.map(lambda so: _run([HIPCC, *FLAGS, "-c", so[0], "-o", so[1]], verbose),
+                    zip(srcs, objs)))
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,155 @@
+// C ABI of libvsa: argument validation on the host, then kernel launches on the
+// caller's stream.  Nothing is launched unless every check passes.
+#include <algorithm>
+
+#include "../../include/vsa.h"
+#include "vsa_internal.h"
+
+namespace {
+
+constexpr int64_t kI32Max = 2147483647;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+vsa_status from_hip(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_HIP; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Common checks of a token-tensor problem (dtype, head_dim, sizes).
+vsa_status check_tokens(int32_t dtype, int64_t batch, int32_t heads, int32_t head_dim, int64_t nq,
+                        int64_t nk, int32_t block_q, int32_t block_k) {
+  if (dtype != VSA_F32 && dtype != VSA_BF16) return VSA_ERR_DTYPE;
+  if (batch <= 0 || heads <= 0 || head_dim <= 0 || nq <= 0 || nk <= 0 || block_q <= 0 ||
+      block_k <= 0)
+    return VSA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return VSA_ERR_UNSUPPORTED;
+  if (nq > kI32Max || nk > kI32Max) return VSA_ERR_SHAPE;
+  if (batch * heads * ceil_div(nq, block_q) > kI32Max) return VSA_ERR_SHAPE;
+  return VSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vsa_status_string(vsa_status s) {
+  switch (s) {
+    case VSA_OK: return "VSA_OK";
+    case VSA_ERR_NULL: return "VSA_ERR_NULL: a required pointer is NULL";
+    case VSA_ERR_SHAPE: return "VSA_ERR_SHAPE: invalid or inconsistent sizes";
+    case VSA_ERR_DTYPE: return "VSA_ERR_DTYPE: dtype must be VSA_F32 or VSA_BF16";
+    case VSA_ERR_PARAM: return "VSA_ERR_PARAM: invalid mask or selection parameter";
+    case VSA_ERR_CAPACITY: return "VSA_ERR_CAPACITY: output capacity or workspace too small";
+    case VSA_ERR_UNSUPPORTED: return "VSA_ERR_UNSUPPORTED: head_dim, alignment or size not supported";
+    case VSA_ERR_HIP: return "VSA_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown vsa_status";
+  }
+}
+
+vsa_status vsa_tile_reorder(const void* src, void* dst, int64_t batch, int32_t T, int32_t H,
+                            int32_t W, int32_t tt, int32_t th, int32_t tw, int64_t row_bytes,
+                            int32_t inverse, hipStream_t stream) {
+  if (!src || !dst) return VSA_ERR_NULL;
+  if (batch <= 0 || T <= 0 || H <= 0 || W <= 0 || tt <= 0 || th <= 0 || tw <= 0 || row_bytes <= 0)
+    return VSA_ERR_SHAPE;
+  if (T % tt || H % th || W % tw) return VSA_ERR_SHAPE;
+  if ((int64_t)T * H * W > kI32Max) return VSA_ERR_SHAPE;
+  if (inverse != 0 && inverse != 1) return VSA_ERR_PARAM;
+  if (row_bytes % 16 || !aligned16(src) || !aligned16(dst)) return VSA_ERR_UNSUPPORTED;
+  if (row_bytes / 16 > kI32Max) return VSA_ERR_UNSUPPORTED;
+  return from_hip(vsa::launch_tile_reorder(src, dst, batch, T, H, W, tt, th, tw, row_bytes, inverse,
+                                           stream));
+}
+
+vsa_status vsa_mask_sta(int32_t T, int32_t H, int32_t W, int32_t tt, int32_t th, int32_t tw,
+                        int32_t wt, int32_t wh, int32_t ww, int32_t* row_ptr, int32_t* col_idx,
+                        int64_t col_capacity, hipStream_t stream) {
+  if (!row_ptr || !col_idx) return VSA_ERR_NULL;
+  if (T <= 0 || H <= 0 || W <= 0 || tt <= 0 || th <= 0 || tw <= 0) return VSA_ERR_SHAPE;
+  if (T % tt || H % th || W % tw) return VSA_ERR_SHAPE;
+  if (wt <= 0 || wh <= 0 || ww <= 0 || wt % 2 == 0 || wh % 2 == 0 || ww % 2 == 0)
+    return VSA_ERR_PARAM;
+  const int64_t NT = T / tt, NH = H / th, NW = W / tw, n = NT * NH * NW;
+  const int64_t bound = n * std::min<int64_t>(wt, NT) * std::min<int64_t>(wh, NH) *
+                        std::min<int64_t>(ww, NW);
+  if (n > kI32Max || bound > kI32Max) return VSA_ERR_SHAPE;
+  if (col_capacity < bound) return VSA_ERR_CAPACITY;
+  return from_hip(vsa::launch_mask_sta((int)NT, (int)NH, (int)NW, wt / 2, wh / 2, ww / 2, row_ptr,
+                                       col_idx, stream));
+}
+
+vsa_status vsa_mask_radial(int32_t T, int32_t S, int32_t block, int32_t* row_ptr,
+                           int32_t* col_idx, int64_t col_capacity, hipStream_t stream) {
+  if (!row_ptr || !col_idx) return VSA_ERR_NULL;
+  if (T <= 0 || S <= 0 || block <= 0) return VSA_ERR_SHAPE;
+  const int64_t N = (int64_t)T * S;
+  if (N > kI32Max - block) return VSA_ERR_SHAPE;
+  const int64_t nb = ceil_div(N, block);
+  if (nb * nb > kI32Max) return VSA_ERR_SHAPE;
+  if (col_capacity < nb * nb) return VSA_ERR_CAPACITY;
+  return from_hip(vsa::launch_mask_radial(T, S, block, row_ptr, col_idx, stream));
+}
+
+vsa_status vsa_mask_nabla(const void* q, const void* k, int32_t dtype, int64_t batch,
+                          int32_t heads, int32_t head_dim, int64_t nq, int64_t nk,
+                          int32_t block_q, int32_t block_k, double scale, const vsa_select* sel,
+                          int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                          void* workspace, size_t* workspace_bytes, hipStream_t stream) {
+  if (!q || !k || !sel || !row_ptr || !col_idx || !workspace_bytes) return VSA_ERR_NULL;
+  vsa_status st = check_tokens(dtype, batch, heads, head_dim, nq, nk, block_q, block_k);
+  if (st != VSA_OK) return st;
+  const int64_t nbq = ceil_div(nq, block_q), nbk = ceil_div(nk, block_k);
+  if (nbk > 4096) return VSA_ERR_UNSUPPORTED;
+  if (!(scale == scale)) return VSA_ERR_PARAM;
+  if (sel->topk < 0 || sel->n_forced < 0 || sel->n_forced > 16) return VSA_ERR_PARAM;
+  if (sel->topk == 0 && !(sel->cdf_threshold > 0.0 && sel->cdf_threshold <= 1.0))
+    return VSA_ERR_PARAM;
+  if (sel->topk > 0 && sel->n_forced > 0) {
+    if (!sel->forced) return VSA_ERR_NULL;
+    for (int r = 0; r < sel->n_forced; ++r) {
+      const int lo = sel->forced[2 * r], hi = sel->forced[2 * r + 1];
+      if (lo < 0 || hi > nbk || lo > hi) return VSA_ERR_PARAM;
+      for (int u = 0; u < r; ++u)  // ranges must be disjoint
+        if (lo < sel->forced[2 * u + 1] && sel->forced[2 * u] < hi) return VSA_ERR_PARAM;
+    }
+  }
+  const int64_t rows = batch * heads * nbq;
+  if (rows * nbk > kI32Max) return VSA_ERR_SHAPE;
+  const size_t need = vsa::nabla_workspace_bytes(batch, heads, head_dim, nq, nk, block_q, block_k);
+  if (!workspace) {
+    *workspace_bytes = need;
+    return VSA_OK;
+  }
+  if (*workspace_bytes < need) return VSA_ERR_CAPACITY;
+  if (col_capacity < rows * nbk) return VSA_ERR_CAPACITY;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(workspace)) return VSA_ERR_UNSUPPORTED;
+  vsa::NablaArgs a{q, k, dtype, batch, heads, head_dim, nq, nk, block_q, block_k, scale,
+                   sel->cdf_threshold, sel->topk, sel->n_forced, sel->forced, row_ptr, col_idx,
+                   workspace};
+  return from_hip(vsa::launch_mask_nabla(a, stream));
+}
+
+vsa_status vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                                     float* lse, int32_t dtype, int64_t batch, int32_t heads,
+                                     int32_t head_dim, int64_t nq, int64_t nk, int32_t block_q,
+                                     int32_t block_k, const int32_t* row_ptr,
+                                     const int32_t* col_idx, int32_t n_slabs, float scale,
+                                     void* workspace, size_t* workspace_bytes,
+                                     hipStream_t stream) {
+  (void)workspace;
+  if (!q || !k || !v || !o || !row_ptr || !col_idx) return VSA_ERR_NULL;
+  vsa_status st = check_tokens(dtype, batch, heads, head_dim, nq, nk, block_q, block_k);
+  if (st != VSA_OK) return st;
+  if (n_slabs != 1 && (int64_t)n_slabs != batch * heads) return VSA_ERR_PARAM;
+  if (!(scale == scale)) return VSA_ERR_PARAM;
+  if (workspace_bytes && !workspace) {  // size query: no workspace needed
+    *workspace_bytes = 0;
+    return VSA_OK;
+  }
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return VSA_ERR_UNSUPPORTED;
+  vsa::AttnArgs a{q, k, v, o, lse, dtype, batch, heads, head_dim, nq, nk, block_q, block_k,
+                  row_ptr, col_idx, n_slabs, scale};
+  return from_hip(vsa::launch_attn_fwd(a, stream));
+}
+
+}  // extern "C"

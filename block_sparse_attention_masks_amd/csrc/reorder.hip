@@ -1,0 +1,77 @@
+// Tile reorder: a gather of whole token rows between raster order and tile-major
+// order (Sliding Tile Attention explainer, aibr.jp/archives/60739, sec. 2-3: work
+// organised per contiguous 3D tile).
+//
+// HBM-bound copy.  One wave owns one destination row at a time: the row index
+// arithmetic is wave-uniform (scalar), and the 64 lanes move the row in 16-byte
+// vectors, so both the read of the source row and the write of the destination
+// row are contiguous 128-bit accesses.
+#include "vsa_internal.h"
+
+namespace vsa {
+namespace {
+
+struct Geometry {
+  int T, H, W, tt, th, tw;
+  int NH, NW, V;  // tile grid extents (h, w) and tokens per tile
+};
+
+// Raster index of the token at tile-major position p.
+__device__ inline int tile_to_raster(int p, const Geometry& g) {
+  const int tile = p / g.V, r = p - tile * g.V;
+  const int it = tile / (g.NH * g.NW), ih = (tile / g.NW) % g.NH, iw = tile % g.NW;
+  const int lt = r / (g.th * g.tw), lh = (r / g.tw) % g.th, lw = r % g.tw;
+  return ((it * g.tt + lt) * g.H + ih * g.th + lh) * g.W + iw * g.tw + lw;
+}
+
+// Tile-major position of raster token n.
+__device__ inline int raster_to_tile(int n, const Geometry& g) {
+  const int t = n / (g.H * g.W), h = (n / g.W) % g.H, w = n % g.W;
+  const int tile = ((t / g.tt) * g.NH + h / g.th) * g.NW + w / g.tw;
+  const int r = ((t % g.tt) * g.th + h % g.th) * g.tw + w % g.tw;
+  return tile * g.V + r;
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWavesPerBlock = 4;
+constexpr int kUnroll = 4;
+
+__global__ __launch_bounds__(kWavesPerBlock * kWave) void tile_reorder_kernel(
+    const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64_t n_rows, int N, int vpr,
+    Geometry g, int inverse) {
+  const int64_t row = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+  if (row >= n_rows) return;
+  const int64_t b = row / N;
+  const int x = (int)(row - b * N);
+  const int from = inverse ? raster_to_tile(x, g) : tile_to_raster(x, g);
+  const u32x4* s = src + (b * N + from) * (int64_t)vpr;
+  u32x4* d = dst + row * (int64_t)vpr;
+  const int l = lane_id();
+  int c = l;
+  for (; c + (kUnroll - 1) * kWave < vpr; c += kUnroll * kWave) {
+    u32x4 t[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) t[u] = __builtin_nontemporal_load(s + c + u * kWave);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) __builtin_nontemporal_store(t[u], d + c + u * kWave);
+  }
+  for (; c < vpr; c += kWave) __builtin_nontemporal_store(__builtin_nontemporal_load(s + c), d + c);
+}
+
+}  // namespace
+
+hipError_t launch_tile_reorder(const void* src, void* dst, int64_t batch, int T, int H, int W,
+                               int tt, int th, int tw, int64_t row_bytes, int inverse,
+                               hipStream_t stream) {
+  Geometry g{T, H, W, tt, th, tw, H / th, W / tw, tt * th * tw};
+  const int N = T * H * W;
+  const int64_t n_rows = batch * N;
+  const int vpr = (int)(row_bytes / 16);
+  const int64_t blocks = (n_rows + kWavesPerBlock - 1) / kWavesPerBlock;
+  hipLaunchKernelGGL(tile_reorder_kernel, dim3((unsigned)blocks), dim3(kWavesPerBlock * kWave), 0,
+                     stream, (const u32x4*)src, (u32x4*)dst, n_rows, N, vpr, g, inverse);
+  return hipGetLastError();
+}
+
+}  // namespace vsa

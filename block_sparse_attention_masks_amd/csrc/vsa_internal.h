@@ -1,0 +1,83 @@
+// Internal declarations shared by the HIP sources of libvsa (not part of the ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vsa {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- wave helpers
+__device__ inline int lane_id() { return __lane_id(); }
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ inline int wave_inclusive_scan(int x) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int y = __shfl_up(x, o, kWave);
+    if (l >= o) x += y;
+  }
+  return x;
+}
+
+// Number of set bits of a 64-bit ballot strictly below this lane.
+__device__ inline int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+// ------------------------------------------------------------- host launchers
+hipError_t launch_tile_reorder(const void* src, void* dst, int64_t batch, int T, int H, int W,
+                               int tt, int th, int tw, int64_t row_bytes, int inverse,
+                               hipStream_t stream);
+
+hipError_t launch_mask_sta(int NT, int NH, int NW, int ht, int hh, int hw, int32_t* row_ptr,
+                           int32_t* col_idx, hipStream_t stream);
+
+hipError_t launch_mask_radial(int T, int S, int block, int32_t* row_ptr, int32_t* col_idx,
+                              hipStream_t stream);
+
+// In-place: row_ptr[1..n] holds per-row counts on entry, absolute offsets on exit.
+hipError_t launch_counts_to_offsets(int32_t* row_ptr, int64_t n_rows, hipStream_t stream);
+
+struct NablaArgs {
+  const void* q;
+  const void* k;
+  int dtype;
+  int64_t batch;
+  int heads, head_dim;
+  int64_t nq, nk;
+  int block_q, block_k;
+  double scale;
+  double threshold;
+  int topk;
+  int n_forced;
+  const int32_t* forced;  // host
+  int32_t* row_ptr;
+  int32_t* col_idx;
+  void* workspace;
+};
+size_t nabla_workspace_bytes(int64_t batch, int heads, int head_dim, int64_t nq, int64_t nk,
+                             int block_q, int block_k);
+hipError_t launch_mask_nabla(const NablaArgs& a, hipStream_t stream);
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int dtype;
+  int64_t batch;
+  int heads, head_dim;
+  int64_t nq, nk;
+  int block_q, block_k;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  int n_slabs;
+  float scale;
+};
+hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace vsa

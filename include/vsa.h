@@ -1,0 +1,199 @@
+/*
+ * vsa.h -- block-sparse softmax attention over a 3D (T x H x W) video-token grid,
+ * for AMD Instinct MI355X (gfx950).  C ABI; plain pointers and sizes.
+ *
+ * The path: make 3D tiles contiguous (vsa_tile_reorder), build a block mask as a
+ * CSR list of kept key blocks (vsa_mask_sta, vsa_mask_radial, vsa_mask_nabla),
+ * then compute exact softmax(Q K^T * scale) V over the kept blocks only
+ * (vsa_block_sparse_attn_fwd).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Token tensors are [batch, n_tokens, heads, head_dim], contiguous, head_dim
+ *   fastest, in device memory.  Tokens are in raster order (t, h, w), w fastest,
+ *   unless they went through vsa_tile_reorder.
+ * - A block is a run of `block` consecutive tokens; the last block of a sequence
+ *   may be ragged.  n_qblocks = ceil(nq / block_q), n_kblocks = ceil(nk / block_k).
+ * - CSR mask: row r lists, in ascending order, the key blocks kept by query block
+ *   r; row_ptr[n_rows + 1] holds absolute int32 offsets into col_idx, both in
+ *   device memory.  A mask shared by all (batch, head) has n_rows = n_qblocks
+ *   ("one slab"); a per-(batch, head) mask has n_rows = batch * heads * n_qblocks
+ *   with row r = (b * heads + h) * n_qblocks + qblock.
+ * - Ownership: the caller owns every buffer.  The library allocates no device
+ *   memory, holds no mutable global state and is reentrant.  Pointers are borrowed
+ *   until the work enqueued on `stream` completes; every call is asynchronous and
+ *   returns once its kernels are enqueued.
+ * - Errors: every argument is validated on the host before anything is launched;
+ *   on error nothing is launched and no output is touched.  A failure reported by
+ *   the HIP runtime at launch maps to VSA_ERR_HIP.  Nothing is printed and no
+ *   exception crosses the ABI.
+ */
+#ifndef VSA_H
+#define VSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t vsa_status;
+#define VSA_OK 0
+#define VSA_ERR_NULL (-1)        /* a required pointer is NULL                              */
+#define VSA_ERR_SHAPE (-2)       /* a size <= 0, inconsistent sizes, grid not divisible     */
+#define VSA_ERR_DTYPE (-3)       /* dtype is not VSA_F32 or VSA_BF16                        */
+#define VSA_ERR_PARAM (-4)       /* even / non-positive window, threshold outside (0, 1],   */
+                                 /* topk < 0, forced range outside [0, n_kblocks], n_slabs  */
+#define VSA_ERR_CAPACITY (-5)    /* col_capacity or workspace too small                     */
+#define VSA_ERR_UNSUPPORTED (-6) /* head_dim not 64 / 128, misaligned pointer or row size   */
+#define VSA_ERR_HIP (-7)         /* the HIP runtime reported an error at launch             */
+
+enum { VSA_F32 = 0, VSA_BF16 = 1 };
+
+/* Human-readable name of a status code (static string). */
+const char* vsa_status_string(vsa_status s);
+
+/*
+ * vsa_tile_reorder -- permute whole token rows between raster order and
+ * tile-major order.
+ *
+ * Sliding Tile Attention explainer (aibr.jp/archives/60739), sec. 2-3: the video
+ * is processed in small rectangular 3D tiles, and organising the work per tile
+ * (instead of per token) cuts memory traffic and redundancy.  Tile-major order
+ * puts the tt*th*tw tokens of each tile next to each other, tiles in raster order
+ * over the (T/tt, H/th, W/tw) tile grid, tokens raster inside a tile.  Position
+ * p = ((it*NH + ih)*NW + iw)*V + (lt*th + lh)*tw + lw holds raster token
+ * ((it*tt + lt)*H + ih*th + lh)*W + iw*tw + lw, with V = tt*th*tw.
+ *
+ * src, dst   device, [batch, T*H*W, row] rows of row_bytes bytes; must not overlap;
+ *            16-byte aligned.
+ * row_bytes  bytes per token row = heads * head_dim * element size; multiple of 16.
+ * inverse    0: raster -> tile-major;  1: tile-major -> raster.
+ * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE (non-positive size, T/H/W not divisible by
+ * tt/th/tw), VSA_ERR_UNSUPPORTED (row_bytes % 16, misalignment), VSA_ERR_HIP.
+ */
+vsa_status vsa_tile_reorder(const void* src, void* dst, int64_t batch,
+                            int32_t T, int32_t H, int32_t W,
+                            int32_t tt, int32_t th, int32_t tw,
+                            int64_t row_bytes, int32_t inverse, hipStream_t stream);
+
+/*
+ * vsa_mask_sta -- sliding 3D tile window (one slab, shared by all batch/heads).
+ *
+ * Sliding Tile Attention explainer (aibr.jp/archives/60739), sec. 3: every query
+ * tile attends the tiles of a window that slides with it (3D locality, sec. 1).
+ * Query tile i keeps key tile j iff |i_t - j_t| <= wt/2, |i_h - j_h| <= wh/2 and
+ * |i_w - j_w| <= ww/2 (tile coordinates; the window is centred and clipped at the
+ * border).  Tiles are numbered in raster order over the tile grid, i.e. block j of
+ * a tile-reordered sequence is tile j; block size = tt*th*tw.
+ *
+ * row_ptr   device, n_tiles + 1 ints;  col_idx  device, col_capacity ints.
+ * col_capacity must be >= n_tiles * min(wt, NT) * min(wh, NH) * min(ww, NW).
+ * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE, VSA_ERR_PARAM (even or non-positive
+ * window), VSA_ERR_CAPACITY, VSA_ERR_HIP.
+ */
+vsa_status vsa_mask_sta(int32_t T, int32_t H, int32_t W, int32_t tt, int32_t th, int32_t tw,
+                        int32_t wt, int32_t wh, int32_t ww,
+                        int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                        hipStream_t stream);
+
+/*
+ * vsa_mask_radial -- energy-decay radial mask over raster order (one slab).
+ *
+ * Radial Attention explainer (aibr.jp/archives/112136), sec. 2-3: dense between
+ * nearby frames; the spatial window shrinks exponentially with temporal distance,
+ * giving O(n log n) kept pairs.  Token pair (q, k), frames f = n / S, in-frame
+ * index s = n % S, d = |f_q - f_k|, r = floor(log2 d): kept iff d <= 1 or
+ * |s_q - s_k| * 2^r < S.  Block pair (I, J) is kept iff any of its token pairs
+ * is.  N = T*S tokens, n_blocks = ceil(N / block) rows and columns.
+ *
+ * row_ptr   device, n_blocks + 1 ints;  col_idx  device, col_capacity ints.
+ * col_capacity must be >= n_blocks * n_blocks (the exact count is only known on
+ * the device).
+ * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE (non-positive sizes, N >= 2^31),
+ * VSA_ERR_CAPACITY, VSA_ERR_HIP.
+ */
+vsa_status vsa_mask_radial(int32_t T, int32_t S, int32_t block,
+                           int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                           hipStream_t stream);
+
+/* Selection rule of vsa_mask_nabla. */
+typedef struct {
+  double cdf_threshold;   /* NABLA cut, in (0, 1]; used when topk == 0           */
+  int32_t topk;           /* > 0: keep the top-k non-forced blocks by pooled logit */
+  int32_t n_forced;       /* number of [lo, hi) key-block ranges always kept      */
+  const int32_t* forced;  /* host array of 2 * n_forced ints (lo0, hi0, lo1, ...)  */
+} vsa_select;
+
+/*
+ * vsa_mask_nabla -- dynamic block mask from mean-pooled Q and K, one slab per
+ * (batch, head).
+ *
+ * NABLA explainer (aibr.jp/archives/124678), sec. 3: Q and K are average-pooled
+ * per block, a small full attention map is computed from the pooled vectors, and
+ * each row is binarised by a threshold on its cumulative distribution; the mask
+ * adapts per sample (sec. 1).  With pooled means Qp (over the valid tokens of
+ * each query block) and Kp, Z = Qp Kp^T * scale and p = softmax(Z) per row (fp64
+ * throughout); the row is sorted by p descending (ties: lower block first) and
+ * the shortest prefix whose running sum reaches cdf_threshold is kept (the
+ * crossing block included; threshold 1 keeps every block).
+ * With topk > 0 (Sparse Forcing summary, gist.science/ja/paper/2604.21221, part
+ * 2: persistent anchors, recent frames, and only the needed past blocks) the
+ * forced ranges are always kept and, of the other blocks, the topk with the
+ * largest Z (ties: lower block first).
+ *
+ * q [batch, nq, heads, head_dim], k [batch, nk, heads, head_dim], device, dtype.
+ * row_ptr   device, batch*heads*n_qblocks + 1 ints;  col_idx device.
+ * col_capacity must be >= batch*heads*n_qblocks*n_kblocks.
+ * workspace device scratch; when workspace == NULL the call only writes the
+ *           required size to *workspace_bytes and returns VSA_OK.
+ * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE, VSA_ERR_DTYPE, VSA_ERR_PARAM,
+ * VSA_ERR_CAPACITY (col_capacity or *workspace_bytes too small),
+ * VSA_ERR_UNSUPPORTED (head_dim, alignment, n_kblocks > 8192), VSA_ERR_HIP.
+ */
+vsa_status vsa_mask_nabla(const void* q, const void* k, int32_t dtype,
+                          int64_t batch, int32_t heads, int32_t head_dim,
+                          int64_t nq, int64_t nk, int32_t block_q, int32_t block_k,
+                          double scale, const vsa_select* sel,
+                          int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                          void* workspace, size_t* workspace_bytes, hipStream_t stream);
+
+/*
+ * vsa_block_sparse_attn_fwd -- exact softmax attention over the kept blocks.
+ *
+ * Every page replaces full 3D attention (all tokens against all tokens, quadratic
+ * cost; Radial Attention explainer sec. 1, Sliding Tile Attention explainer sec.
+ * 1, NABLA explainer sec. 1) by attention over a subset of blocks, computed
+ * head-wise (SPADE summary, gist.science/ja/paper/2608.03335, "The solution" part
+ * 3).  For a query token of block i with kept key blocks J_i:
+ *   o = sum_j softmax_j(q . k_j * scale) v_j over every valid token of J_i,
+ *   lse = ln sum_j exp(q . k_j * scale).
+ * A row with no kept block gives o = 0 and lse = -inf.  bf16 inputs are
+ * multiplied on the matrix cores with fp32 accumulation and the probabilities are
+ * rounded to bf16 before P V; fp32 inputs stay fp32 throughout.
+ *
+ * q, o [batch, nq, heads, head_dim]; k, v [batch, nk, heads, head_dim]; device,
+ * dtype, 16-byte aligned.  lse: NULL or device [batch, heads, nq] fp32.
+ * row_ptr/col_idx: CSR with n_slabs = 1 (shared) or batch*heads slabs.
+ * workspace / workspace_bytes as for vsa_mask_nabla (the current kernels need
+ * none: the query returns 0 and NULL is accepted).
+ * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE, VSA_ERR_DTYPE, VSA_ERR_PARAM (n_slabs),
+ * VSA_ERR_UNSUPPORTED (head_dim not 64/128, misalignment), VSA_ERR_CAPACITY,
+ * VSA_ERR_HIP.  The CSR contents are trusted: column indices must lie in
+ * [0, n_kblocks) and row_ptr must be non-decreasing.
+ */
+vsa_status vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                                     float* lse, int32_t dtype, int64_t batch, int32_t heads,
+                                     int32_t head_dim, int64_t nq, int64_t nk,
+                                     int32_t block_q, int32_t block_k,
+                                     const int32_t* row_ptr, const int32_t* col_idx,
+                                     int32_t n_slabs, float scale,
+                                     void* workspace, size_t* workspace_bytes,
+                                     hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VSA_H */

@@ -1,0 +1,146 @@
+"""C-ABI contract tests that need no GPU: the library loads, exports every call
+the header declares, and rejects bad arguments on the host before any launch.
+
+Every call below either fails validation or is a workspace-size query, so no
+kernel is ever launched and the (fake, non-null) pointers are never touched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_masks_amd as vsa
+from block_sparse_attention_masks_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x1000)      # 16-byte aligned, never dereferenced
+ODD = ctypes.c_void_p(0x1008)       # misaligned
+NULL = ctypes.c_void_p(0)
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_PARAM, E_CAP, E_UNSUP = 0, -1, -2, -3, -4, -5, -6
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libvsa.so is not built (run __graft_entry__.build())")
+    return vsa.lib()
+
+
+def test_exports_match_header(L):
+    with open(os.path.join(ROOT, "include", "vsa.h")) as f:
+        header = f.read()
+    declared = set(re.findall(r"^(?:vsa_status|const char\*)\s+(vsa_\w+)\(", header, re.M))
+    assert declared == set(vsa.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name)
+
+
+def test_status_strings(L):
+    for code in range(-7, 1):
+        s = vsa.status_string(code)
+        assert s.startswith("VSA_")
+    assert "unknown" in vsa.status_string(-99)
+
+
+def reorder(L, src=FAKE, dst=FAKE, batch=1, grid=(4, 8, 8), tile=(2, 4, 4), row_bytes=256, inverse=0):
+    return L.vsa_tile_reorder(src, dst, batch, *grid, *tile, row_bytes, inverse, NULL)
+
+
+def test_reorder_validation(L):
+    assert reorder(L, src=NULL) == E_NULL
+    assert reorder(L, dst=NULL) == E_NULL
+    assert reorder(L, batch=0) == E_SHAPE
+    assert reorder(L, grid=(5, 8, 8)) == E_SHAPE
+    assert reorder(L, tile=(2, 0, 4)) == E_SHAPE
+    assert reorder(L, inverse=2) == E_PARAM
+    assert reorder(L, row_bytes=24) == E_UNSUP
+    assert reorder(L, src=ODD) == E_UNSUP
+    assert reorder(L, grid=(2048, 2048, 1024), tile=(1, 1, 1)) == E_SHAPE
+
+
+def sta(L, grid=(8, 16, 16), tile=(4, 4, 4), window=(1, 3, 3), rp=FAKE, ci=FAKE, cap=10 ** 6):
+    return L.vsa_mask_sta(*grid, *tile, *window, rp, ci, cap, NULL)
+
+
+def test_sta_validation(L):
+    assert sta(L, rp=NULL) == E_NULL
+    assert sta(L, ci=NULL) == E_NULL
+    assert sta(L, grid=(8, 16, 15)) == E_SHAPE
+    assert sta(L, window=(2, 3, 3)) == E_PARAM
+    assert sta(L, window=(1, 3, 0)) == E_PARAM
+    assert sta(L, cap=32 * 9 - 1) == E_CAP          # bound = 32 tiles * 1*3*3
+
+
+def radial(L, T=5, S=64, block=16, rp=FAKE, ci=FAKE, cap=10 ** 6):
+    return L.vsa_mask_radial(T, S, block, rp, ci, cap, NULL)
+
+
+def test_radial_validation(L):
+    assert radial(L, rp=NULL) == E_NULL
+    assert radial(L, T=0) == E_SHAPE
+    assert radial(L, block=-1) == E_SHAPE
+    assert radial(L, cap=20 * 20 - 1) == E_CAP
+    assert radial(L, T=125, S=3600, block=1) == E_SHAPE   # nb^2 overflows int32
+
+
+def nabla(L, q=FAKE, k=FAKE, dtype=1, B=1, H=2, D=128, nq=1000, nk=900, bq=64, bk=64, scale=0.1,
+          thr=0.8, topk=0, forced=(), rp=FAKE, ci=FAKE, cap=10 ** 8, ws=FAKE, nbytes=None):
+    sel, keep = _lib._select(thr, topk, forced)
+    nb = ctypes.c_size_t(10 ** 12 if nbytes is None else nbytes)
+    st = L.vsa_mask_nabla(q, k, dtype, B, H, D, nq, nk, bq, bk, scale, ctypes.byref(sel), rp, ci, cap,
+                          ws, ctypes.byref(nb), NULL)
+    return st, nb.value
+
+
+def test_nabla_validation(L):
+    assert nabla(L, q=NULL)[0] == E_NULL
+    assert nabla(L, dtype=2)[0] == E_DTYPE
+    assert nabla(L, D=96)[0] == E_UNSUP
+    assert nabla(L, nq=0)[0] == E_SHAPE
+    assert nabla(L, thr=0.0)[0] == E_PARAM
+    assert nabla(L, thr=1.5)[0] == E_PARAM
+    assert nabla(L, topk=-1)[0] == E_PARAM
+    assert nabla(L, topk=4, forced=[(0, 3), (2, 5)])[0] == E_PARAM        # overlapping
+    assert nabla(L, topk=4, forced=[(0, 30)])[0] == E_PARAM               # past n_kblocks (15)
+    assert nabla(L, nk=64 * 5000)[0] == E_UNSUP
+    assert nabla(L, nbytes=0)[0] == E_CAP
+    assert nabla(L, cap=2 * 16 * 15 - 1)[0] == E_CAP
+    assert nabla(L, q=ODD)[0] == E_UNSUP
+
+
+def test_nabla_workspace_query(L):
+    st, need = nabla(L, ws=NULL, nbytes=0)
+    assert st == OK
+    # pooled Q (2 heads x 16 blocks x 128 fp64), pooled K (2 x 15 x 128), map
+    # (2 x 16 x 15 fp64), bitmap (32 rows x 1 word), each 256-byte aligned
+    expect = sum(-(-x // 256) * 256 for x in (2 * 16 * 128 * 8, 2 * 15 * 128 * 8, 2 * 16 * 15 * 8, 32 * 4))
+    assert need == expect
+
+
+def attn(L, q=FAKE, k=FAKE, v=FAKE, o=FAKE, dtype=1, B=1, H=2, D=128, nq=100, nk=100, bq=64, bk=64,
+         rp=FAKE, ci=FAKE, slabs=1, scale=0.1, ws=FAKE, query=False):
+    nb = ctypes.c_size_t(123)
+    st = L.vsa_block_sparse_attn_fwd(q, k, v, o, NULL, dtype, B, H, D, nq, nk, bq, bk, rp, ci, slabs,
+                                     scale, NULL if query else ws, ctypes.byref(nb) if query else None, NULL)
+    return st, nb.value
+
+
+def test_attn_validation(L):
+    assert attn(L, v=NULL)[0] == E_NULL
+    assert attn(L, rp=NULL)[0] == E_NULL
+    assert attn(L, dtype=7)[0] == E_DTYPE
+    assert attn(L, D=32)[0] == E_UNSUP
+    assert attn(L, nk=-1)[0] == E_SHAPE
+    assert attn(L, bq=0)[0] == E_SHAPE
+    assert attn(L, slabs=3)[0] == E_PARAM
+    assert attn(L, scale=float("nan"))[0] == E_PARAM
+    assert attn(L, o=ODD)[0] == E_UNSUP
+    assert attn(L, query=True) == (OK, 0)
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 64, 2, 8)
+    with pytest.raises(ValueError):
+        vsa.vsa_tile_reorder(x, (4, 4, 4), (2, 2, 2))

@@ -1,0 +1,164 @@
+"""GPU parity of each library call on small synthetic problems (all rows compared).
+
+Every case goes through the C ABI (via the ctypes binding) and is compared with
+the fp64 oracle on the same inputs: masks and reorders bit-exactly, attention to
+the bf16 tolerance (max-abs 2e-2, mean-abs 2e-3) or 1e-4 for fp32."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_masks_amd as vsa
+import oracle
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+BF16_MAX, BF16_MEAN, F32_MAX = 2e-2, 2e-3, 1e-4
+
+
+def to_np(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def csr_np(rp, ci):
+    rp = rp.cpu().numpy()
+    return rp, ci[: int(rp[-1])].cpu().numpy()
+
+
+def rand(shape, dtype, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g, dtype=torch.float64) * scale).to(dtype)
+
+
+# --------------------------------------------------------------------- reorder
+@pytest.mark.parametrize("grid,tile,heads,dim,dtype", [
+    ((8, 16, 16), (4, 4, 4), 2, 64, torch.float32),
+    ((6, 16, 24), (6, 8, 8), 3, 128, torch.bfloat16),
+    ((4, 8, 16), (1, 8, 8), 5, 128, torch.bfloat16),
+    ((3, 5, 7), (1, 1, 7), 1, 8, torch.bfloat16),      # 16-byte rows
+])
+def test_tile_reorder_bit_exact(grid, tile, heads, dim, dtype):
+    n = int(np.prod(grid))
+    x = rand((2, n, heads, dim), dtype, 1)
+    y = vsa.vsa_tile_reorder(x.to(DEV), grid, tile)
+    want = oracle.tile_reorder(x.numpy() if dtype == torch.float32 else x.view(torch.int16).numpy(), grid, tile)
+    got = y.cpu()
+    got = got.numpy() if dtype == torch.float32 else got.view(torch.int16).numpy()
+    assert np.array_equal(got, want)
+    back = vsa.vsa_tile_reorder(y, grid, tile, inverse=True)
+    assert torch.equal(back.cpu(), x)
+
+
+# ----------------------------------------------------------------------- masks
+@pytest.mark.parametrize("grid,tile,window", [
+    ((8, 16, 16), (4, 4, 4), (1, 3, 3)), ((30, 48, 80), (6, 8, 8), (3, 3, 5)),
+    ((1, 3, 3), (1, 1, 1), (1, 3, 3)), ((12, 12, 12), (2, 2, 2), (5, 3, 7)),
+    ((8, 16, 16), (4, 4, 4), (3, 7, 7)), ((2, 2, 2), (2, 2, 2), (1, 1, 1)),
+])
+def test_mask_sta_bit_exact(grid, tile, window):
+    rp, ci = csr_np(*vsa.vsa_mask_sta(grid, tile, window, DEV))
+    orp, oci = oracle.mask_sta(grid, tile, window)
+    assert np.array_equal(rp, orp) and np.array_equal(ci, oci)
+
+
+@pytest.mark.parametrize("T,S,block", [(5, 8, 2), (3, 10, 4), (9, 7, 5), (12, 16, 8), (6, 5, 13),
+                                       (17, 4, 3), (1, 9, 4), (16, 20, 32), (40, 300, 64),
+                                       (33, 1000, 128), (2, 100, 7)])
+def test_mask_radial_bit_exact(T, S, block):
+    rp, ci = csr_np(*vsa.vsa_mask_radial(T, S, block, DEV))
+    orp, oci = oracle.mask_radial(T, S, block)
+    assert np.array_equal(rp, orp) and np.array_equal(ci, oci)
+
+
+def _compare_selected(rp, ci, orp, oci, exempt):
+    bad = []
+    for r in range(len(orp) - 1):
+        a, b = ci[rp[r]:rp[r + 1]], oci[orp[r]:orp[r + 1]]
+        if not np.array_equal(a, b) and not exempt[r]:
+            bad.append(r)
+    return bad
+
+
+@pytest.mark.parametrize("nq,nk,bq,bk,thr,dtype", [
+    (2048, 2048, 64, 64, 0.9, torch.float32), (1000, 777, 64, 32, 0.5, torch.bfloat16),
+    (300, 4100, 50, 16, 0.95, torch.bfloat16), (129, 129, 128, 1, 0.7, torch.float32),
+    (500, 500, 64, 64, 1.0, torch.bfloat16),
+])
+def test_mask_nabla_bit_exact(nq, nk, bq, bk, thr, dtype):
+    q = rand((1, nq, 3, 128), dtype, 2, 1.0)
+    k = rand((1, nk, 3, 128), dtype, 3, 1.0)
+    q[..., :8] += 2.0 * torch.linspace(-1, 1, nq).reshape(1, nq, 1, 1).to(dtype)   # some structure
+    k[..., :8] += 2.0 * torch.linspace(-1, 1, nk).reshape(1, nk, 1, 1).to(dtype)
+    scale = 128 ** -0.5
+    rp, ci = csr_np(*vsa.vsa_mask_nabla(q.to(DEV), k.to(DEV), bq, bk, scale, threshold=thr))
+    orp, oci, flagged, ties = oracle.mask_nabla(to_np(q), to_np(k), bq, bk, scale, thr)
+    assert len(rp) == len(orp)
+    bad = _compare_selected(rp, ci, orp, oci, flagged | ties)
+    assert not bad, f"rows differing outside the flagged set: {bad[:10]}"
+
+
+def test_mask_topk_forced_bit_exact():
+    q = rand((2, 700, 2, 128), torch.bfloat16, 4)
+    k = rand((2, 3000, 2, 128), torch.bfloat16, 5)
+    forced = [(0, 5), (40, 47)]
+    rp, ci = csr_np(*vsa.vsa_mask_nabla(q.to(DEV), k.to(DEV), 64, 64, 0.1, topk=6, forced=forced))
+    orp, oci, ties = oracle.mask_ar(to_np(q), to_np(k), 64, 64, 0.1, 6, forced)
+    assert not _compare_selected(rp, ci, orp, oci, ties)
+    assert set(np.diff(rp).tolist()) == {18}
+
+
+# ------------------------------------------------------------------- attention
+def _check(o_gpu, lse_gpu, o_ref, lse_ref, dtype):
+    o = to_np(o_gpu)
+    err = np.abs(o - o_ref)
+    if dtype == torch.float32:
+        assert err.max() <= F32_MAX, err.max()
+    else:
+        assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN, (err.max(), err.mean())
+    lse = lse_gpu.cpu().double().numpy()
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lse), fin)
+    assert np.abs(lse[fin] - lse_ref[fin]).max() < (1e-4 if dtype == torch.float32 else 2e-2)
+
+
+CASES = [
+    # nq, nk, heads, D, bq, bk, density, slabs, dtype
+    (256, 256, 2, 128, 64, 64, 1.0, 1, torch.bfloat16),
+    (1000, 1000, 3, 128, 128, 128, 0.4, 1, torch.bfloat16),
+    (777, 1234, 2, 128, 384, 384, 0.6, 2, torch.bfloat16),       # ragged q and k tails
+    (500, 900, 2, 64, 100, 70, 0.5, 2, torch.bfloat16),          # blocks not multiples of 64
+    (130, 4100, 1, 128, 64, 64, 0.2, 1, torch.bfloat16),         # nq != nk, long keys
+    (300, 300, 2, 128, 300, 1, 0.3, 2, torch.bfloat16),          # one-token key blocks
+    (2048, 2048, 2, 64, 64, 64, 0.5, 2, torch.float32),
+    (200, 333, 2, 128, 32, 48, 0.5, 1, torch.float32),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[str(i) for i in range(len(CASES))])
+def test_attention_parity(case):
+    nq, nk, H, D, bq, bk, dens, slabs, dtype = case
+    scale = D ** -0.5
+    q, k, v = rand((1, nq, H, D), dtype, 10), rand((1, nk, H, D), dtype, 11), rand((1, nk, H, D), dtype, 12)
+    nbq, nbk = -(-nq // bq), -(-nk // bk)
+    rng = np.random.default_rng(13)
+    keep = rng.random((slabs * nbq, nbk)) < dens
+    keep[np.arange(slabs * nbq), rng.integers(0, nbk, size=slabs * nbq)] = True
+    if slabs * nbq > 2:
+        keep[1] = False                                           # an empty row
+    rp, ci = oracle.csr_from_bool(keep)
+    o_ref, lse_ref = oracle.attention(to_np(q), to_np(k), to_np(v), rp, ci, bq, bk, scale, slabs)
+    o, lse = vsa.vsa_block_sparse_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV),
+                                           torch.from_numpy(rp).to(DEV), torch.from_numpy(ci).to(DEV),
+                                           bq, bk, slabs, scale)
+    _check(o, lse, o_ref, lse_ref, dtype)
+
+
+def test_attention_deterministic_and_dense_mask():
+    q, k, v = (rand((1, 1500, 2, 128), torch.bfloat16, s).to(DEV) for s in (20, 21, 22))
+    rp, ci = vsa.all_ones_mask(-(-1500 // 128), -(-1500 // 128), DEV)
+    o1, l1 = vsa.vsa_block_sparse_attn_fwd(q, k, v, rp, ci, 128, 128)
+    o2, l2 = vsa.vsa_block_sparse_attn_fwd(q, k, v, rp, ci, 128, 128)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        *(t.double().cpu().permute(0, 2, 1, 3) for t in (q, k, v))).permute(0, 2, 1, 3)
+    err = (o1.double().cpu() - ref).abs()
+    assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN

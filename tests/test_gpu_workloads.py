@@ -1,0 +1,207 @@
+"""GPU parity at the five workloads' full sizes, through the whole path.
+
+Each test runs the path the benchmark times (tile reorder -> mask -> attention ->
+inverse reorder) on the seeded synthetic inputs, compares the mask with the fp64
+oracle in full (bit-exact; NABLA / top-k rows whose decision sits within rounding
+of the cut are flagged, counted and exempt), and compares the output with the
+oracle fed the GPU's own mask: every row for the small workloads, 4,096 sampled
+(head, query) rows for the three large ones."""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_masks_amd as vsa
+import oracle
+from workloads import gen
+from workloads.configs import CONFIGS
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+BF16_MAX, BF16_MEAN, F32_MAX = 2e-2, 2e-3, 1e-4
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+def csr_np(rp, ci):
+    rp = rp.cpu().numpy()
+    return rp, ci[: int(rp[-1])].cpu().numpy()
+
+
+def _compare_masks(rp, ci, orp, oci, exempt):
+    assert len(rp) == len(orp)
+    bad = [r for r in range(len(orp) - 1)
+           if not np.array_equal(ci[rp[r]:rp[r + 1]], oci[orp[r]:orp[r + 1]]) and not exempt[r]]
+    n_diff_exempt = sum(1 for r in np.nonzero(exempt)[0]
+                        if not np.array_equal(ci[rp[r]:rp[r + 1]], oci[orp[r]:orp[r + 1]]))
+    return bad, n_diff_exempt
+
+
+def _sampled_rows_check(name, x_cpu, o_gpu, rp, ci, block_q, block_k, n_slabs, perm=None, n_rows=4096):
+    """Oracle output of sampled (b, h, raster query token) rows vs the GPU output.
+
+    perm (tile-major position -> raster token) describes the order the attention
+    ran in; the oracle reorders its own copies of Q, K, V with it."""
+    cfg = CONFIGS[name]
+    D = cfg["head_dim"]
+    scale = D ** -0.5
+    rows = gen.sample_rows(name, n_rows)
+    o_cpu = o_gpu.cpu()
+    nbq = -(-x_cpu["q"].shape[1] // block_q)
+    inv = None if perm is None else np.argsort(perm)
+    errs = []
+    for h in np.unique(rows[:, 1]):
+        sel = rows[rows[:, 1] == h]
+        b = 0
+        qh = x_cpu["q"][b, :, h].double().numpy()
+        kh = x_cpu["k"][b, :, h].double().numpy()
+        vh = x_cpu["v"][b, :, h].double().numpy()
+        if perm is not None:
+            qh, kh, vh = qh[perm], kh[perm], vh[perm]
+        toks = sel[:, 2]
+        pos = toks if inv is None else inv[toks]          # row position in the attention order
+        base = 0 if n_slabs == 1 else (b * cfg["heads"] + h) * nbq
+        o_ref, _ = oracle.attention_rows(qh[pos], pos, kh, vh, rp, ci, base, block_q, block_k, scale)
+        got = o_cpu[b, toks, h].double().numpy()
+        errs.append(np.abs(got - o_ref))
+    err = np.concatenate(errs)
+    return err.max(), err.mean()
+
+
+def _run_path(x, grid, tile, mask_fn, block, n_slabs):
+    """reorder (if tiled) -> mask -> attention -> inverse reorder, on the GPU."""
+    qd, kd, vd = (x[w].to(DEV) for w in ("q", "k", "v"))
+    if tile is not None:
+        qd, kd, vd = (vsa.vsa_tile_reorder(t, grid, tile) for t in (qd, kd, vd))
+    rp, ci = mask_fn(qd, kd)
+    o, lse = vsa.vsa_block_sparse_attn_fwd(qd, kd, vd, rp, ci, block, block, n_slabs)
+    if tile is not None:
+        o = vsa.vsa_tile_reorder(o, grid, tile, inverse=True)
+    torch.cuda.synchronize()
+    return o, rp, ci
+
+
+# ------------------------------------------------------------------------ tiny
+@pytest.mark.parametrize("variant", ["dense", "sta", "nabla"])
+def test_tiny_fp32(variant):
+    cfg = CONFIGS["tiny"]
+    grid, tile = cfg["grid"], cfg["tile"]
+    x = gen.make_inputs("tiny")
+    xq, xk, xv = (oracle.tile_reorder(x[w].double().numpy(), grid, tile) for w in ("q", "k", "v"))
+    scale = 64 ** -0.5
+    if variant == "dense":
+        fn, slabs = (lambda q, k: vsa.all_ones_mask(32, 32, DEV)), 1
+        orp, oci = oracle.mask_all(32, 32)
+        exempt = np.zeros(32, bool)
+    elif variant == "sta":
+        fn, slabs = (lambda q, k: vsa.vsa_mask_sta(grid, tile, cfg["sta_window"], DEV)), 1
+        orp, oci = oracle.mask_sta(grid, tile, cfg["sta_window"])
+        exempt = np.zeros(32, bool)
+    else:
+        thr = cfg["nabla_threshold"]
+        fn, slabs = (lambda q, k: vsa.vsa_mask_nabla(q, k, 64, 64, scale, threshold=thr)), 2
+        orp, oci, fl, nt = oracle.mask_nabla(xq, xk, 64, 64, scale, thr)
+        exempt = fl | nt
+    o, rp_d, ci_d = _run_path(x, grid, tile, fn, 64, slabs)
+    rp, ci = csr_np(rp_d, ci_d)
+    bad, _ = _compare_masks(rp, ci, orp, oci, exempt)
+    assert not bad
+    o_ref, _ = oracle.attention(xq, xk, xv, rp, ci, 64, 64, scale, slabs)
+    o_ref = oracle.tile_reorder(o_ref, grid, tile, inverse=True)
+    err = np.abs(o.cpu().double().numpy() - o_ref)
+    log(f"tiny/{variant}: nnz={len(ci)} max_abs={err.max():.2e} mean_abs={err.mean():.2e}")
+    assert err.max() <= F32_MAX
+
+
+# ------------------------------------------------------------------------- sta
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+def test_sta_workload():
+    cfg = CONFIGS["sta"]
+    grid, tile, window = cfg["grid"], cfg["tile"], cfg["window"]
+    t0 = time.time()
+    x = gen.make_inputs("sta")
+    log(f"sta: inputs {time.time() - t0:.1f}s")
+    o, rp_d, ci_d = _run_path(x, grid, tile, lambda q, k: vsa.vsa_mask_sta(grid, tile, window, DEV), 384, 1)
+    rp, ci = csr_np(rp_d, ci_d)
+    orp, oci = oracle.mask_sta(grid, tile, window)
+    assert np.array_equal(rp, orp) and np.array_equal(ci, oci) and len(ci) == 9152
+    perm = oracle.tile_order_source(grid, tile)
+    mx, mn = _sampled_rows_check("sta", x, o, rp, ci, 384, 384, 1, perm=perm)
+    log(f"sta: 4096 rows max_abs={mx:.2e} mean_abs={mn:.2e} ({time.time() - t0:.1f}s)")
+    assert mx <= BF16_MAX and mn <= BF16_MEAN
+
+
+# ----------------------------------------------------------------------- nabla
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_nabla_workload():
+    cfg = CONFIGS["nabla"]
+    grid, tile, thr = cfg["grid"], cfg["tile"], cfg["threshold"]
+    scale = 128 ** -0.5
+    t0 = time.time()
+    x = gen.make_inputs("nabla")
+    log(f"nabla: inputs {time.time() - t0:.1f}s")
+    fn = lambda q, k: vsa.vsa_mask_nabla(q, k, 64, 64, scale, threshold=thr)
+    o, rp_d, ci_d = _run_path(x, grid, tile, fn, 64, 40)
+    rp, ci = csr_np(rp_d, ci_d)
+    perm = oracle.tile_order_source(grid, tile)
+    qt = x["q"][:, perm].double().numpy()
+    kt = x["k"][:, perm].double().numpy()
+    orp, oci, fl, nt = oracle.mask_nabla(qt, kt, 64, 64, scale, thr)
+    del qt, kt
+    bad, n_ex = _compare_masks(rp, ci, orp, oci, fl | nt)
+    dens = np.diff(rp).reshape(40, 960).sum(axis=1) / (960 * 960)
+    log(f"nabla: flagged rows {int(fl.sum())}, near-tie rows {int(nt.sum())}, flagged rows that differ {n_ex}, "
+        f"density per head min {dens.min():.3f} max {dens.max():.3f} (sparsity {1 - dens.mean():.3f})")
+    assert not bad, f"unflagged mismatching rows: {bad[:10]}"
+    mx, mn = _sampled_rows_check("nabla", x, o, rp, ci, 64, 64, 40, perm=perm)
+    log(f"nabla: 4096 rows max_abs={mx:.2e} mean_abs={mn:.2e} ({time.time() - t0:.1f}s)")
+    assert mx <= BF16_MAX and mn <= BF16_MEAN
+
+
+# ---------------------------------------------------------------------- radial
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_radial_workload():
+    cfg = CONFIGS["radial"]
+    T, H, W = cfg["grid"]
+    S, block = H * W, cfg["block"]
+    t0 = time.time()
+    x = gen.make_inputs("radial")
+    log(f"radial: inputs {time.time() - t0:.1f}s")
+    o, rp_d, ci_d = _run_path(x, None, None, lambda q, k: vsa.vsa_mask_radial(T, S, block, DEV), block, 1)
+    rp, ci = csr_np(rp_d, ci_d)
+    orp, oci = oracle.mask_radial(T, S, block)
+    assert np.array_equal(rp, orp) and np.array_equal(ci, oci) and len(ci) == 2718652
+    mx, mn = _sampled_rows_check("radial", x, o, rp, ci, block, block, 1)
+    log(f"radial: 4096 rows max_abs={mx:.2e} mean_abs={mn:.2e} ({time.time() - t0:.1f}s)")
+    assert mx <= BF16_MAX and mn <= BF16_MEAN
+
+
+# ---------------------------------------------------------------------- ar
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+def test_ar_chunk_workload():
+    cfg = CONFIGS["ar"]
+    T, H, W = cfg["grid"]
+    block, topk = cfg["block"], cfg["topk"]
+    scale = 128 ** -0.5
+    forced = vsa.ar_forced_ranges(H * W, T, cfg["anchor_frames"], cfg["recent_frames"], block)
+    assert forced == oracle.ar_forced_ranges(H * W, T, cfg["anchor_frames"], cfg["recent_frames"], block)
+    x = gen.make_inputs("ar")
+    fn = lambda q, k: vsa.vsa_mask_nabla(q, k, block, block, scale, topk=topk, forced=forced)
+    o, rp_d, ci_d = _run_path(x, None, None, fn, block, 12)
+    rp, ci = csr_np(rp_d, ci_d)
+    xq, xk, xv = (x[w].double().numpy() for w in ("q", "k", "v"))
+    orp, oci, ties = oracle.mask_ar(xq, xk, block, block, scale, topk, forced)
+    bad, n_ex = _compare_masks(rp, ci, orp, oci, ties)
+    log(f"ar: near-tie rows {int(ties.sum())}, of which differ {n_ex}")
+    assert not bad and set(np.diff(rp).tolist()) == {115}
+    o_ref, _ = oracle.attention(xq, xk, xv, rp, ci, block, block, scale, 12)
+    err = np.abs(o.cpu().double().numpy() - o_ref)
+    log(f"ar: all rows max_abs={err.max():.2e} mean_abs={err.mean():.2e}")
+    assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN
