@@ -2,11 +2,12 @@
 
 A step is one pass of the whole path over one batch of synthetic input, all on
 the GPU with the inputs resident in HBM:
-    tile reorder of Q, K, V -> STA mask -> block-sparse attention -> inverse
-    reorder of O
-on the STA workload (24 heads, head_dim 128, bf16, 30x48x80 = 115,200 tokens,
-6x8x8 tiles = 384-token blocks on a 5x6x10 tile grid, 3x3x5 tile window clipped
-at the border).
+    [tile reorder of Q, K, V] -> block mask -> block-sparse attention ->
+    [inverse reorder of O]
+The default workload is the STA one (24 heads, head_dim 128, bf16, 30x48x80 =
+115,200 tokens, 6x8x8 tiles = 384-token blocks on a 5x6x10 tile grid, 3x3x5 tile
+window clipped at the border); --workload nabla | radial | ar measures the
+others (their lines are reports, not the headline).
 
 value       = kept-block attention FLOPs (4 * D * sum of nq*nk over kept block
               pairs, true token counts) / wall time of a step, TFLOP/s.
@@ -15,9 +16,10 @@ roofline    = the attention kernel alone: the same FLOPs / its mean launch time
               MFMA peak (2.5 PFLOP/s).
 speedup     = the same kernel on an all-ones mask (dense attention) / sparse.
 cpu_baseline= the fp64 oracle on a bounded sample (the same path for a subset of
-              heads), FLOPs counted the same way.
+              heads), FLOPs counted the same way (STA workload only).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-dense] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sta]
+                       [--no-dense] [--no-cpu]
 """
 import argparse
 import hashlib
@@ -33,11 +35,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
-PEAK_HBM_GBS = 8000.0
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 METRIC = "block-sparse attn effective TFLOPS (kept blocks), % bf16 MFMA peak; speedup vs dense"
-WORKLOAD = "sta"
 ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_masks_amd", "csrc", "attn_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_sta_traffic.json")
+
+DESCRIPTION = {
+    "sta": "sta: 1 x 24 heads x 115,200 tokens (30x48x80 grid), head_dim 128, bf16, 6x8x8 tiles "
+           "(384-token blocks), 3x3x5 tile window clipped at the border",
+    "nabla": "nabla: 1 x 40 heads x 61,440 tokens (16x48x80 grid), head_dim 128, bf16, 1x8x8 tiles "
+             "(64-token blocks), pooled-map CDF threshold 0.8, per-head masks",
+    "radial": "radial: 1 x 24 heads x 450,000 tokens (125x45x80 grid, 3,600 per frame), head_dim 128, "
+              "bf16, raster 128-token blocks, radial energy-decay mask",
+    "ar": "ar: 1 x 12 heads, 4,680 query tokens (3x30x52 chunk) over a 32,760-token KV cache "
+          "(21x30x52), head_dim 128, bf16, 64-token blocks, anchors + last 3 frames + top-16",
+}
 
 
 def attn_flops(rp, ci, block_q, block_k, nq, nk, D, bh, n_slabs):
@@ -89,11 +101,83 @@ def cpu_baseline(x, cfg, target_s=12.0):
                       f"{len(os.sched_getaffinity(0))} cores available"}
 
 
+class Path:
+    """Device buffers and the calls of one workload's path (no allocation per step)."""
+
+    def __init__(self, name, cfg, x, dev):
+        import block_sparse_attention_masks_amd as vsa
+        self.vsa, self.name, self.dev = vsa, name, dev
+        B, H, D = cfg["batch"], cfg["heads"], cfg["head_dim"]
+        self.B, self.H, self.D = B, H, D
+        self.q, self.k, self.v = (x[w].to(dev) for w in ("q", "k", "v"))
+        self.nq, self.nk = self.q.shape[1], self.k.shape[1]
+        self.scale = D ** -0.5
+        self.tiled = None
+        if name in ("sta", "nabla"):
+            self.tiled = (cfg["grid"], cfg["tile"])
+            t = cfg["tile"]
+            self.bq = self.bk = t[0] * t[1] * t[2]
+            self.qa, self.ka, self.va, self.oa = (torch.empty_like(self.q) for _ in range(4))
+        else:
+            self.bq = self.bk = cfg["block"]
+            self.qa, self.ka, self.va = self.q, self.k, self.v
+            self.oa = torch.empty_like(self.q)
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((B, H, self.nq), dtype=torch.float32, device=dev)
+        nbq, nbk = -(-self.nq // self.bq), -(-self.nk // self.bk)
+        self.nbq, self.nbk = nbq, nbk
+        self.n_slabs = 1 if name in ("sta", "radial") else B * H
+        rows = self.n_slabs * nbq
+        self.rp = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+        if name == "sta":
+            cap = vsa.sta_capacity(cfg["grid"], cfg["tile"], cfg["window"])
+            self.mask = lambda: vsa.vsa_mask_sta(cfg["grid"], cfg["tile"], cfg["window"], dev,
+                                                 row_ptr=self.rp, col_idx=self.ci)
+        elif name == "radial":
+            T, Hg, Wg = cfg["grid"]
+            cap = nbq * nbk
+            self.mask = lambda: vsa.vsa_mask_radial(T, Hg * Wg, self.bq, dev, row_ptr=self.rp,
+                                                    col_idx=self.ci)
+        else:
+            cap = rows * nbk
+            if name == "nabla":
+                sel = dict(threshold=cfg["threshold"])
+            else:
+                T, Hg, Wg = cfg["grid"]
+                forced = vsa.ar_forced_ranges(Hg * Wg, T, cfg["anchor_frames"], cfg["recent_frames"],
+                                              self.bk)
+                sel = dict(topk=cfg["topk"], forced=forced)
+            ws = torch.empty(vsa.nabla_workspace_bytes(self.qa, self.ka, self.bq, self.bk, self.scale,
+                                                       sel.get("threshold", 1.0), sel.get("topk", 0),
+                                                       sel.get("forced", ())),
+                             dtype=torch.uint8, device=dev)
+            self.mask = lambda: vsa.vsa_mask_nabla(self.qa, self.ka, self.bq, self.bk, self.scale,
+                                                   workspace=ws, row_ptr=self.rp, col_idx=self.ci,
+                                                   **sel)
+        self.ci = torch.empty(cap, dtype=torch.int32, device=dev)
+
+    def reorder_in(self):
+        if self.tiled:
+            for src, dst in ((self.q, self.qa), (self.k, self.ka), (self.v, self.va)):
+                self.vsa.vsa_tile_reorder(src, *self.tiled, out=dst)
+
+    def attn(self, rp=None, ci=None):
+        self.vsa.vsa_block_sparse_attn_fwd(self.qa, self.ka, self.va, self.rp if rp is None else rp,
+                                           self.ci if ci is None else ci, self.bq, self.bk,
+                                           self.n_slabs if rp is None else 1, self.scale,
+                                           out=self.oa, lse=self.lse)
+
+    def reorder_out(self):
+        if self.tiled:
+            self.vsa.vsa_tile_reorder(self.oa, *self.tiled, inverse=True, out=self.o)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="sta", choices=sorted(DESCRIPTION))
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -103,47 +187,27 @@ def main():
               "with no communication and multi-GPU runs are not part of this build.", file=sys.stderr)
         sys.exit(2)
 
-    import block_sparse_attention_masks_amd as vsa
     from workloads import gen
     from workloads.configs import CONFIGS
 
-    cfg = CONFIGS[WORKLOAD]
-    grid, tile, window = cfg["grid"], cfg["tile"], cfg["window"]
-    H, D = cfg["heads"], cfg["head_dim"]
-    block = tile[0] * tile[1] * tile[2]
+    name = args.workload
+    cfg = CONFIGS[name]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t_gen = time.perf_counter()
-    x = gen.make_inputs(WORKLOAD)
-    print(f"[bench] inputs generated in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
-    q, k, v = (x[w].to(dev) for w in ("q", "k", "v"))
-    N = q.shape[1]
+    x = gen.make_inputs(name)
+    print(f"[bench] {name}: inputs generated in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    path = Path(name, cfg, x, dev)
     stream = torch.cuda.current_stream(dev)
-    qt, kt, vt, ot = (torch.empty_like(q) for _ in range(4))
-    o = torch.empty_like(q)
-    lse = torch.empty((1, H, N), dtype=torch.float32, device=dev)
-    nbq = N // block
-    cap = vsa.sta_capacity(grid, tile, window)
-    rp = torch.empty(nbq + 1, dtype=torch.int32, device=dev)
-    ci = torch.empty(cap, dtype=torch.int32, device=dev)
-
-    ev = {name: [] for name in ("reorder_qkv", "mask", "attn", "reorder_o")}
+    stages = ("reorder_in", "mask", "attn", "reorder_out")
+    ev = {s: [] for s in stages}
 
     def step(record):
         marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
-        if record:
-            marks[0].record(stream)
-        for src, dst in ((q, qt), (k, kt), (v, vt)):
-            vsa.vsa_tile_reorder(src, grid, tile, out=dst)
-        if record:
-            marks[1].record(stream)
-        vsa.vsa_mask_sta(grid, tile, window, dev, row_ptr=rp, col_idx=ci)
-        if record:
-            marks[2].record(stream)
-        vsa.vsa_block_sparse_attn_fwd(qt, kt, vt, rp, ci, block, block, 1, out=ot, lse=lse)
-        if record:
-            marks[3].record(stream)
-        vsa.vsa_tile_reorder(ot, grid, tile, inverse=True, out=o)
+        for i, fn in enumerate((path.reorder_in, path.mask, path.attn, path.reorder_out)):
+            if record:
+                marks[i].record(stream)
+            fn()
         if record:
             marks[4].record(stream)
         return marks
@@ -158,47 +222,49 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     for m in all_marks:
-        for i, name in enumerate(ev):
-            ev[name].append(m[i].elapsed_time(m[i + 1]))
+        for i, s in enumerate(stages):
+            ev[s].append(m[i].elapsed_time(m[i + 1]))
     ms_step = wall * 1e3 / args.steps
 
-    rp_h = rp.cpu().numpy()
-    ci_h = ci[: int(rp_h[-1])].cpu().numpy()
-    flops = attn_flops(rp_h, ci_h, block, block, N, N, D, H, 1)
+    rp_h = path.rp.cpu().numpy()
+    ci_h = path.ci[: int(rp_h[-1])].cpu().numpy()
+    flops = attn_flops(rp_h, ci_h, path.bq, path.bk, path.nq, path.nk, path.D, path.B * path.H, path.n_slabs)
     attn_ms = float(np.mean(ev["attn"]))
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
-    print(f"[bench] step {ms_step:.3f} ms; per-kernel ms: " +
+    print(f"[bench] step {ms_step:.3f} ms; per-stage ms: " +
           ", ".join(f"{k_}={np.mean(v_):.3f}" for k_, v_ in ev.items()), file=sys.stderr, flush=True)
 
     dense = None
     if not args.no_dense:
-        drp, dci = vsa.all_ones_mask(nbq, nbq, dev)
+        drp, dci = path.vsa.all_ones_mask(path.nbq, path.nbk, dev)
+        path.attn(drp, dci)
         dms = []
-        vsa.vsa_block_sparse_attn_fwd(qt, kt, vt, drp, dci, block, block, 1, out=ot, lse=lse)
         for _ in range(args.dense_reps):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            vsa.vsa_block_sparse_attn_fwd(qt, kt, vt, drp, dci, block, block, 1, out=ot, lse=lse)
+            path.attn(drp, dci)
             b.record(stream)
             b.synchronize()
             dms.append(a.elapsed_time(b))
-        dense_flops = 4.0 * D * N * N * H
+        dense_flops = 4.0 * path.D * path.nq * path.nk * path.B * path.H
         dense = {"ms": float(np.mean(dms)), "tflops": dense_flops / (np.mean(dms) * 1e-3) / 1e12,
                  "speedup_vs_dense": float(np.mean(dms)) / attn_ms}
         print(f"[bench] dense run {dense['ms']:.2f} ms ({dense['tflops']:.1f} TFLOP/s)", file=sys.stderr, flush=True)
 
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
+    if name == "sta" and os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if tr.get("attn_src_sha256_16") == source_hash(ATTN_SRC):
             traffic = tr.get("bytes_per_launch")
 
     cpu = None
-    if not args.no_cpu:
+    if name == "sta" and not args.no_cpu:
         cpu = cpu_baseline(x, cfg)
         print(f"[bench] cpu baseline {cpu['value']:.4f} TFLOP/s ({cpu['sample']})", file=sys.stderr, flush=True)
 
+    token_bytes = path.q.numel() * path.q.element_size()
+    reorder_ms = float(np.mean(ev["reorder_in"]) + np.mean(ev["reorder_out"]))
     out = {
         "metric": METRIC,
         "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
@@ -212,14 +278,14 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "sta: 1 x 24 heads x 115,200 tokens (30x48x80 grid), head_dim 128, bf16, "
-                               "6x8x8 tiles (384-token blocks), 3x3x5 tile window clipped at the border",
-                   "global_batch": 1, "seq_len": N, "heads": H, "head_dim": D, "block": block,
-                   "kept_block_pairs": int(len(ci_h)), "kept_fraction": round(len(ci_h) / nbq ** 2, 5),
+        "config": {"workload": DESCRIPTION[name], "global_batch": path.B, "seq_len": path.nq,
+                   "kv_len": path.nk, "heads": path.H, "head_dim": path.D, "block": path.bq,
+                   "mask_slabs": path.n_slabs, "kept_block_pairs": int(len(ci_h)),
+                   "kept_fraction": round(len(ci_h) / (path.n_slabs * path.nbq * path.nbk), 5),
                    "parallelism": "none (one GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "attn_fwd_bf16_kernel<128>",
+                     "traffic": traffic, "kernel": f"attn_fwd_bf16_kernel<{path.D}>",
                      "flops_per_launch": flops, "ms_per_launch": round(attn_ms, 4)},
         "cpu_baseline": cpu,
         "attn_tflops": round(attn_tflops, 2),
@@ -227,8 +293,9 @@ def main():
         "speedup_vs_dense": None if dense is None else round(dense["speedup_vs_dense"], 3),
         "dense_ms": None if dense is None else round(dense["ms"], 3),
         "dense_tflops": None if dense is None else round(dense["tflops"], 2),
-        "kernel_ms": {k_: round(float(np.mean(v_)), 4) for k_, v_ in ev.items()},
-        "reorder_gbs": round(4 * 2 * q.numel() * 2 / (np.sum([np.mean(ev["reorder_qkv"]), np.mean(ev["reorder_o"])]) * 1e-3) / 1e9, 1),
+        "stage_ms": {k_: round(float(np.mean(v_)), 4) for k_, v_ in ev.items()},
+        "mask_over_attn": round(float(np.mean(ev["mask"])) / attn_ms, 5),
+        "reorder_gbs": (round(4 * 2 * token_bytes / (reorder_ms * 1e-3) / 1e9, 1) if path.tiled else None),
     }
     print(json.dumps(out), flush=True)
 

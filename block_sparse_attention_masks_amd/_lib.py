@@ -163,9 +163,10 @@ def nabla_workspace_bytes(q, k, block_q, block_k, scale=None, threshold=1.0, top
 
 
 def vsa_mask_nabla(q, k, block_q, block_k, scale=None, threshold=None, topk=0, forced=(),
-                   workspace=None):
+                   workspace=None, row_ptr=None, col_idx=None):
     """NABLA (threshold) or anchor + recent + top-k (topk > 0) mask, one slab per
-    (batch, head) -> (row_ptr, col_idx)."""
+    (batch, head) -> (row_ptr, col_idx).  Preallocated outputs and workspace may be
+    passed (see nabla_workspace_bytes)."""
     _require(q, "q")
     _require(k, "k", q.device)
     B, nq, Hh, D = q.shape
@@ -174,15 +175,21 @@ def vsa_mask_nabla(q, k, block_q, block_k, scale=None, threshold=None, topk=0, f
     sel, _keep = _select(threshold, topk, forced)
     nbq, nbk = -(-nq // block_q), -(-nk // block_k)
     rows = B * Hh * nbq
-    row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=q.device)
-    col_idx = torch.empty(rows * nbk, dtype=torch.int32, device=q.device)
-    need = nabla_workspace_bytes(q, k, block_q, block_k, scale, sel.cdf_threshold, topk, forced)
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
+    if row_ptr is None:
+        row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=q.device)
+    if col_idx is None:
+        col_idx = torch.empty(rows * nbk, dtype=torch.int32, device=q.device)
+    _require(row_ptr, "row_ptr", q.device)
+    _require(col_idx, "col_idx", q.device)
+    if row_ptr.numel() != rows + 1 or row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise ValueError("row_ptr must be int32 [batch*heads*n_qblocks + 1] and col_idx int32")
+    if workspace is None:
+        need = nabla_workspace_bytes(q, k, block_q, block_k, scale, sel.cdf_threshold, topk, forced)
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     nbytes = ctypes.c_size_t(workspace.numel() * workspace.element_size())
     _check(lib().vsa_mask_nabla(_ptr(q), _ptr(k), _DTYPE[q.dtype], B, Hh, D, nq, nk, block_q,
                                 block_k, float(scale), ctypes.byref(sel), _ptr(row_ptr),
-                                _ptr(col_idx), rows * nbk, _ptr(workspace), ctypes.byref(nbytes),
+                                _ptr(col_idx), col_idx.numel(), _ptr(workspace), ctypes.byref(nbytes),
                                 _stream(q)), "vsa_mask_nabla")
     return row_ptr, col_idx
 

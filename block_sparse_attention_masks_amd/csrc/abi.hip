@@ -1,5 +1,7 @@
 // C ABI of libvsa: argument validation on the host, then kernel launches on the
 // caller's stream.  Nothing is launched unless every check passes.
+#include <math.h>
+
 #include <algorithm>
 
 #include "../../include/vsa.h"
@@ -141,7 +143,7 @@ vsa_status vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v
   vsa_status st = check_tokens(dtype, batch, heads, head_dim, nq, nk, block_q, block_k);
   if (st != VSA_OK) return st;
   if (n_slabs != 1 && (int64_t)n_slabs != batch * heads) return VSA_ERR_PARAM;
-  if (!(scale == scale)) return VSA_ERR_PARAM;
+  if (!(scale > 0.0f) || scale == INFINITY) return VSA_ERR_PARAM;
   if (workspace_bytes && !workspace) {  // size query: no workspace needed
     *workspace_bytes = 0;
     return VSA_OK;

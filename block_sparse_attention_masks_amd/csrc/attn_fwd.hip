@@ -4,20 +4,24 @@
 // pages' masks decide which blocks are kept).
 //
 // bf16 path (matrix cores).  A workgroup of 4 waves owns 128 query rows of one
-// (batch, head, query block); each wave owns 32 of them.  For every kept key
-// block the workgroup walks 64-key tiles:
-//   * K and V tiles go HBM -> LDS (16-byte loads); V is stored transposed,
-//     V^T[d][key], with the keys of each 16-key group permuted (quads 1 and 2
-//     swapped) so that the probabilities come out of the S accumulators in
-//     exactly the operand layout of the P V product;
+// (batch, head, query block); each wave owns 32 of them, held in registers as
+// the B operand of S^T = K Q^T.  The kept key blocks are walked as one stream of
+// 64-key tiles:
+//   * tile t+1 is fetched from HBM into registers (16-byte loads) while tile t is
+//     computed from LDS; the registers are then written to the other half of a
+//     double-buffered LDS stage, so each tile costs one barrier;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (M = keys, N = queries, K = head
-//     dim).  The accumulator of a 32x32 tile gives each lane one query column
-//     and 16 keys, so the row max / row sum are in-lane plus one exchange
-//     between the two half-waves;
-//   * online softmax in the log2 domain (scale * log2(e) folded in), running max
-//     and sum per query, rescale of the output accumulator;
+//     dim): the accumulator gives each lane one query and 16 keys, so the row max
+//     and row sum are in-lane plus one exchange between the half-waves;
+//   * online softmax in the log2 domain with a lazy reference maximum: the
+//     output is rescaled only when a row's maximum grows by more than 2^8, which
+//     keeps every exponent <= 2^8 and leaves the normalised result unchanged;
 //   * O^T += V^T P^T on the same instruction (M = head dim, N = queries, K =
-//     keys), P rounded to bf16.
+//     keys), P rounded to bf16; the row sum adds the rounded values, so the
+//     weights applied to V are exactly normalised.  V stays row-major in LDS; ds_read_b64_tr_b16
+//     delivers each lane its 8 keys of one head-dim column.  The key order inside
+//     each 16-key group follows the S accumulator layout (lane half g holds keys
+//     4g..4g+3 and 8+4g..8+4g+3), so P feeds the product without any shuffle.
 // Ragged key tails are masked with -inf; query rows past the block or the
 // sequence are computed but never stored.  A row with no kept block writes 0
 // and lse = -inf.
@@ -32,39 +36,70 @@ namespace vsa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 128;      // query rows per workgroup
 constexpr int kBN = 64;       // keys per tile
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kKPad = 8;      // bf16 padding per K row in LDS
-constexpr int kVPad = 8;      // bf16 padding per V^T row in LDS
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale slack (exponents stay <= 2^8)
 
 struct Work {
   int64_t items, per_xcd;
   int nbq, mt_per_qb;
 };
 
-// Position of key `o` (0..15 inside a 16-key group) in the V^T row: quads 1 and 2
-// trade places.  Lane half g of the P V product holds keys {4g..4g+3, 8+4g..8+4g+3}
-// of the group as its 8 consecutive operand elements.
-__device__ inline int vt_slot(int o) {
-  const int q4 = o >> 2, r4 = o & 3;
-  const int pq = (q4 == 1) ? 2 : (q4 == 2 ? 1 : q4);
-  return pq * 4 + r4;
-}
+// LDS row pitches (elements).  K rows shift by 4 banks (conflict-free 16-byte
+// reads of 16 consecutive rows); V rows shift by 16 banks (conflict-free
+// transposed 8-byte reads of 4 consecutive rows x 64 bytes).
+template <int D> struct Pitch;
+template <> struct Pitch<128> { static constexpr int K = 136, V = 160; };
+template <> struct Pitch<64> { static constexpr int K = 72, V = 96; };
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(
+struct Smem {
+  uint16_t k[2][kBN * Pitch<D>::K];
+  uint16_t v[2][kBN * Pitch<D>::V];
+};
+
+// Stream of 64-key tiles over the kept blocks of one CSR row (wave-uniform).
+struct TileIter {
+  const int32_t* col;
+  int e, e1;
+  int64_t k0, ke;
+  int block_k;
+  int64_t nk;
+  __device__ bool valid() const { return e < e1; }
+  __device__ void open() {  // position on the first tile of block col[e]
+    if (e < e1) {
+      const int64_t ks = (int64_t)col[e] * block_k;
+      k0 = ks;
+      ke = min(ks + block_k, nk);
+    }
+  }
+  __device__ void next() {
+    k0 += kBN;
+    if (k0 >= ke) {
+      ++e;
+      open();
+    }
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
     int64_t nq, int64_t nk, int heads, int block_q, int block_k,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int n_slabs,
     float scale_log2, Work wk) {
-  __shared__ __attribute__((aligned(16))) uint16_t sk[kBN][D + kKPad];
-  __shared__ __attribute__((aligned(16))) uint16_t svt[D][kBN + kVPad];
+  __shared__ __attribute__((aligned(16))) Smem<D> sm;
+  constexpr int kPer = kBN * D / 8 / kThreads;  // 16-byte chunks per thread per tensor
 
   // XCD-aware mapping: workgroups are dealt round-robin to the 8 XCDs; give each
   // XCD a contiguous range of work items so that the query tiles of one query
@@ -85,7 +120,53 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(
 
   const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
   const int col = l & 31, g = l >> 5;
-  const int64_t row_stride = (int64_t)heads * D;  // elements between tokens
+  const int row_stride = heads * D;  // elements between tokens (validated < 2^31 / 64)
+
+  const int64_t slab = n_slabs == 1 ? 0 : b * heads + h;
+  const int64_t r = slab * wk.nbq + qb;
+  TileIter it{col_idx, row_ptr[r], row_ptr[r + 1], 0, 0, block_k, nk};
+  it.open();
+
+  const uint16_t* kbase = k + (b * nk * heads + h) * (int64_t)D;
+  const uint16_t* vbase = v + (b * nk * heads + h) * (int64_t)D;
+
+  // This thread stages chunks tid + 256 i of each tile: key row krow0 + kRowStep*i,
+  // head-dim columns d8 .. d8+7 (the same for every tile).
+  constexpr int kRowStep = kThreads / (D / 8);
+  const int krow0 = tid / (D / 8), d8 = (tid % (D / 8)) * 8;
+  const int goff0 = krow0 * row_stride + d8;
+  const int soff_k = krow0 * Pitch<D>::K + d8, soff_v = krow0 * Pitch<D>::V + d8;
+  u32x4 kreg[kPer], vreg[kPer];
+  auto load = [&](const TileIter& t) {
+    const uint16_t* kb = kbase + t.k0 * row_stride + goff0;
+    const uint16_t* vb = vbase + t.k0 * row_stride + goff0;
+    const int nv = (int)min((int64_t)kBN, t.ke - t.k0);
+    if (nv == kBN) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        kreg[i] = *(const u32x4*)(kb + i * kRowStep * row_stride);
+        vreg[i] = *(const u32x4*)(vb + i * kRowStep * row_stride);
+      }
+    } else {  // ragged tail: rows past the block read as zero
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const bool ok = krow0 + i * kRowStep < nv;
+        kreg[i] = ok ? *(const u32x4*)(kb + i * kRowStep * row_stride) : u32x4{0, 0, 0, 0};
+        vreg[i] = ok ? *(const u32x4*)(vb + i * kRowStep * row_stride) : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store = [&](int bufi) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      *(u32x4*)(sm.k[bufi] + soff_k + i * kRowStep * Pitch<D>::K) = kreg[i];
+      *(u32x4*)(sm.v[bufi] + soff_v + i * kRowStep * Pitch<D>::V) = vreg[i];
+    }
+  };
+  if (it.valid()) {
+    load(it);
+    store(0);
+  }
 
   // Q fragments (B operand of S^T = K Q^T): query col, dims 16*s + 8*g .. +7.
   const int64_t my_q = q_lo + w * 32 + col;
@@ -95,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(
     const uint16_t* qp = q + ((b * nq + (ok ? my_q : q_lo)) * heads + h) * D + 8 * g;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      uint4 u = ok ? *(const uint4*)(qp + 16 * s) : make_uint4(0, 0, 0, 0);
+      u32x4 u = ok ? *(const u32x4*)(qp + 16 * s) : u32x4{0, 0, 0, 0};
       qf[s] = __builtin_bit_cast(bf16x8, u);
     }
   }
@@ -105,94 +186,108 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(
   for (int t = 0; t < D / 32; ++t)
 #pragma unroll
     for (int a = 0; a < 16; ++a) acc_o[t][a] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // transposed-read lane address inside a V tile: key row 4g + j, columns
+  // 16*((l/16)%2) + 4c (plus 32t and 16kk rows per product step)
+  const int vt_off = (4 * g + ((l & 15) >> 2)) * Pitch<D>::V + 16 * ((l >> 4) & 1) + 4 * (l & 3);
+  const int k_off = col * Pitch<D>::K + 8 * g;
 
-  const int64_t slab = n_slabs == 1 ? 0 : b * heads + h;
-  const int64_t r = slab * wk.nbq + qb;
-  const int e0 = row_ptr[r], e1 = row_ptr[r + 1];
+  // Ragged tiles are masked through the initial value of the S accumulators:
+  // bias = 0 for keys below the tile's valid count and -inf past it, so a key past
+  // the tail scores -inf.  The biases change only when the valid count does.
+  f32x16 bias0, bias1;
+#pragma unroll
+  for (int a = 0; a < 16; ++a) bias0[a] = bias1[a] = 0.f;
+  int bias_valid = kBN;
 
-  const uint16_t* kbase = k + (b * nk * heads + h) * (int64_t)D;
-  const uint16_t* vbase = v + (b * nk * heads + h) * (int64_t)D;
-
-  for (int e = e0; e < e1; ++e) {
-    const int j = col_idx[e];
-    const int64_t ks = (int64_t)j * block_k;
-    const int64_t ke = min(ks + block_k, nk);
-    for (int64_t k0 = ks; k0 < ke; k0 += kBN) {
-      // ---- stage K and V^T tiles in LDS
-      constexpr int kChunks = kBN * D / 8;  // 16-byte chunks per tile
+  // One 64-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
+  auto tile = [&](const uint16_t* sk, const uint16_t* sv) {
+    f32x16 s0 = bias0, s1 = bias1;
 #pragma unroll
-      for (int c = tid; c < kChunks; c += kThreads) {
-        const int kr = c / (D / 8), d8 = (c % (D / 8)) * 8;
-        const int64_t key = k0 + kr;
-        uint4 ku = make_uint4(0, 0, 0, 0), vu = make_uint4(0, 0, 0, 0);
-        if (key < ke) {
-          ku = *(const uint4*)(kbase + key * row_stride + d8);
-          vu = *(const uint4*)(vbase + key * row_stride + d8);
-        }
-        *(uint4*)&sk[kr][d8] = ku;
-        const int slot = (kr & ~15) + vt_slot(kr & 15);
-        const uint16_t* vh = (const uint16_t*)&vu;
+    for (int kd = 0; kd < D / 16; ++kd) {
+      const bf16x8 a0 = *(const bf16x8*)(sk + k_off + 16 * kd);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kd], s0, 0, 0, 0);
+    }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) svt[d8 + i][slot] = vh[i];
-      }
-      __syncthreads();
-
-      // ---- S^T = K Q^T for two 32-key sub-tiles
-      f32x16 s[2];
+    for (int kd = 0; kd < D / 16; ++kd) {
+      const bf16x8 a1 = *(const bf16x8*)(sk + k_off + 32 * Pitch<D>::K + 16 * kd);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kd], s1, 0, 0, 0);
+    }
+    float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-#pragma unroll
-        for (int a = 0; a < 16; ++a) s[st][a] = 0.f;
-#pragma unroll
-        for (int kd = 0; kd < D / 16; ++kd) {
-          const bf16x8 af = *(const bf16x8*)&sk[32 * st + col][16 * kd + 8 * g];
-          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[kd], s[st], 0, 0, 0);
-        }
-      }
-
-      // ---- online softmax (log2 domain)
-      const int valid = (int)min((int64_t)kBN, ke - k0);
-      float mt_ = -INFINITY;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int a = 0; a < 16; ++a) {
-          const int key = 32 * st + 8 * (a >> 2) + 4 * g + (a & 3);
-          const float x = key < valid ? s[st][a] * scale_log2 : -INFINITY;
-          s[st][a] = x;
-          mt_ = fmaxf(mt_, x);
-        }
-      mt_ = fmaxf(mt_, __shfl_xor(mt_, 32, kWave));
-      const float m_new = fmaxf(m_run, mt_);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      float psum = 0.f;
-      bf16x8 pf[4];
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int a = 0; a < 16; ++a) {
-          const float p = __builtin_amdgcn_exp2f(s[st][a] - m_new);
-          psum += p;
-          pf[2 * st + (a >> 3)][a & 7] = (__bf16)p;
-        }
-      l_run = l_run * alpha + psum;
+    for (int a = 1; a < 16; ++a) mx = fmaxf(fmaxf(mx, s0[a]), s1[a]);  // v_max3
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * scale_log2;
+    const bool grow = mx > m_ref + kRescaleLog2;
+    if (__ballot(grow)) {
+      // a real branch: keeps the compiler from turning the rare rescale into an
+      // unconditional multiply by a selected factor
+      asm volatile("" ::: "memory");
+      const float m_new = grow ? mx : m_ref;
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int t = 0; t < D / 32; ++t)
 #pragma unroll
         for (int a = 0; a < 16; ++a) acc_o[t][a] *= alpha;
-
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 vf = *(const bf16x8*)&svt[32 * t + col][16 * kk + 8 * g];
-          acc_o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], acc_o[t], 0, 0, 0);
-        }
-      __syncthreads();
     }
+    bf16x8 pf[4];
+#pragma unroll
+    for (int a = 0; a < 16; ++a) {
+      pf[a >> 3][a & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s0[a], scale_log2, -m_ref));
+      pf[2 + (a >> 3)][a & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s1[a], scale_log2, -m_ref));
+    }
+    // row sum of the rounded weights (so the weights applied to V sum to exactly 1)
+    float psum = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x2* pp = (const bf16x2*)&pf[kk];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) psum = __builtin_amdgcn_fdot2_f32_bf16(pp[i], ones, psum, false);
+    }
+    l_run += psum;
+
+    // O^T += V^T P^T; A operand (V^T) by transposed LDS reads: lane (j = (l%16)/4,
+    // c = l%4) addresses key row 16kk+4g+j (+8 for the second half) at head-dim
+    // columns 32t + 16*((l/16)%2) + 4c .. +3.
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) {
+        const uint16_t* p0 = sv + vt_off + 16 * kk * Pitch<D>::V + 32 * t;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (s16x4 __attribute__((address_space(3)))*)(p0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (s16x4 __attribute__((address_space(3)))*)(p0 + 8 * Pitch<D>::V));
+        const s16x4 vv[2] = {lo, hi};
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, vv);
+        acc_o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], acc_o[t], 0, 0, 0);
+      }
+    }
+  };
+  __syncthreads();
+
+  int buf = 0;
+  while (it.valid()) {
+    const int valid = (int)min((int64_t)kBN, it.ke - it.k0);
+    TileIter nx = it;
+    nx.next();
+    if (nx.valid()) load(nx);
+    if (__builtin_expect(valid != bias_valid, 0)) {
+      bias_valid = valid;
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const int key = 8 * (a >> 2) + 4 * g + (a & 3);
+        bias0[a] = key < valid ? 0.f : -INFINITY;
+        bias1[a] = key + 32 < valid ? 0.f : -INFINITY;
+      }
+    }
+    tile(sm.k[buf], sm.v[buf]);
+    if (nx.valid()) store(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    it = nx;
   }
 
   // ---- epilogue
@@ -205,7 +300,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         const int d = 32 * t + 8 * a4 + 4 * g;
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
         bf16x4 ov;
 #pragma unroll
         for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(acc_o[t][4 * a4 + i] * inv);
@@ -213,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(
       }
     if (lse != nullptr && g == 0)
       lse[(b * heads + h) * nq + my_q] =
-          l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f : -INFINITY;
+          l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f : -INFINITY;
   }
 }
 

@@ -177,9 +177,10 @@ vsa_status vsa_mask_nabla(const void* q, const void* k, int32_t dtype,
  * q, o [batch, nq, heads, head_dim]; k, v [batch, nk, heads, head_dim]; device,
  * dtype, 16-byte aligned.  lse: NULL or device [batch, heads, nq] fp32.
  * row_ptr/col_idx: CSR with n_slabs = 1 (shared) or batch*heads slabs.
+ * scale: finite and > 0 (the usual 1/sqrt(head_dim)).
  * workspace / workspace_bytes as for vsa_mask_nabla (the current kernels need
  * none: the query returns 0 and NULL is accepted).
- * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE, VSA_ERR_DTYPE, VSA_ERR_PARAM (n_slabs),
+ * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE, VSA_ERR_DTYPE, VSA_ERR_PARAM (n_slabs, scale),
  * VSA_ERR_UNSUPPORTED (head_dim not 64/128, misalignment), VSA_ERR_CAPACITY,
  * VSA_ERR_HIP.  The CSR contents are trusted: column indices must lie in
  * [0, n_kblocks) and row_ptr must be non-decreasing.

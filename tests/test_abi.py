@@ -135,6 +135,7 @@ def test_attn_validation(L):
     assert attn(L, bq=0)[0] == E_SHAPE
     assert attn(L, slabs=3)[0] == E_PARAM
     assert attn(L, scale=float("nan"))[0] == E_PARAM
+    assert attn(L, scale=-0.1)[0] == E_PARAM
     assert attn(L, o=ODD)[0] == E_UNSUP
     assert attn(L, query=True) == (OK, 0)
 
