@@ -91,7 +91,13 @@ struct TileIter {
   }
 };
 
-template <int D>
+// Value held by lane l ^ 32 (the other half-wave), via v_permlane32_swap (no LDS).
+__device__ inline float xchg32(float x, int g) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(g == 0 ? r[1] : r[0]);
+}
+
+template <int D, int KS>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
@@ -100,6 +106,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     float scale_log2, Work wk) {
   __shared__ __attribute__((aligned(16))) Smem<D> sm;
   constexpr int kPer = kBN * D / 8 / kThreads;  // 16-byte chunks per thread per tensor
+  // KS = 1: the 4 waves own 32 query rows each and all 64 keys of every tile.
+  // KS = 2 (query blocks of <= 64 rows): waves w and w+2 own the same 32 rows and
+  // split every tile's keys in halves; their softmax states merge at the end.
+  constexpr int BM = kBM / KS;   // query rows per workgroup
+  constexpr int NST = 2 / KS;    // 32-key sub-tiles per wave per tile
 
   // XCD-aware mapping: workgroups are dealt round-robin to the 8 XCDs; give each
   // XCD a contiguous range of work items so that the query tiles of one query
@@ -114,12 +125,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const int h = (int)(rest % heads);
   const int64_t b = rest / heads;
 
-  const int64_t q_lo = (int64_t)qb * block_q + (int64_t)mt * kBM;
-  const int64_t q_hi = min(min((int64_t)(qb + 1) * block_q, nq), q_lo + kBM);
+  const int64_t q_lo = (int64_t)qb * block_q + (int64_t)mt * BM;
+  const int64_t q_hi = min(min((int64_t)(qb + 1) * block_q, nq), q_lo + BM);
   if (q_lo >= q_hi) return;
 
   const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
   const int col = l & 31, g = l >> 5;
+  const int qw = KS == 1 ? w : (w & 1);   // this wave's 32-row query group
+  const int kh = KS == 1 ? 0 : (w >> 1);  // this wave's key half (KS = 2)
   const int row_stride = heads * D;  // elements between tokens (validated < 2^31 / 64)
 
   const int64_t slab = n_slabs == 1 ? 0 : b * heads + h;
@@ -169,7 +182,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   }
 
   // Q fragments (B operand of S^T = K Q^T): query col, dims 16*s + 8*g .. +7.
-  const int64_t my_q = q_lo + w * 32 + col;
+  const int64_t my_q = q_lo + qw * 32 + col;
   bf16x8 qf[D / 16];
   {
     const bool ok = my_q < q_hi;
@@ -193,31 +206,56 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const int vt_off = (4 * g + ((l & 15) >> 2)) * Pitch<D>::V + 16 * ((l >> 4) & 1) + 4 * (l & 3);
   const int k_off = col * Pitch<D>::K + 8 * g;
 
-  // Ragged tiles are masked through the initial value of the S accumulators:
-  // bias = 0 for keys below the tile's valid count and -inf past it, so a key past
-  // the tail scores -inf.  The biases change only when the valid count does.
-  f32x16 bias0, bias1;
+  // One 64-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  `valid` < 64
+  // only for the ragged last tile of a block.
+  auto tile = [&](const uint16_t* sk, const uint16_t* sv, int valid) {
+    f32x16 s[NST];
 #pragma unroll
-  for (int a = 0; a < 16; ++a) bias0[a] = bias1[a] = 0.f;
-  int bias_valid = kBN;
-
-  // One 64-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
-  auto tile = [&](const uint16_t* sk, const uint16_t* sv) {
-    f32x16 s0 = bias0, s1 = bias1;
+    for (int st = 0; st < NST; ++st)
 #pragma unroll
-    for (int kd = 0; kd < D / 16; ++kd) {
-      const bf16x8 a0 = *(const bf16x8*)(sk + k_off + 16 * kd);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kd], s0, 0, 0, 0);
+      for (int a = 0; a < 16; ++a) s[st][a] = 0.f;
+    {
+      // K fragments are read kLook steps ahead of the products that use them
+      constexpr int kSteps = D / 16, kLook = 2;
+      const uint16_t* kp = sk + k_off + 32 * kh * Pitch<D>::K;
+      bf16x8 fr[kSteps][NST];
+#pragma unroll
+      for (int kd = 0; kd < kLook; ++kd)
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+          fr[kd][st] = *(const bf16x8*)(kp + 32 * st * Pitch<D>::K + 16 * kd);
+#pragma unroll
+      for (int kd = 0; kd < kSteps; ++kd) {
+        if (kd + kLook < kSteps) {
+#pragma unroll
+          for (int st = 0; st < NST; ++st)
+            fr[kd + kLook][st] = *(const bf16x8*)(kp + 32 * st * Pitch<D>::K + 16 * (kd + kLook));
+        }
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[kd][st], qf[kd], s[st], 0, 0, 0);
+      }
     }
+    if (valid < kBN) {
+      // a real branch (kept out of the full-tile path): keys past the tail score -inf
+      asm volatile("" ::: "memory");
 #pragma unroll
-    for (int kd = 0; kd < D / 16; ++kd) {
-      const bf16x8 a1 = *(const bf16x8*)(sk + k_off + 32 * Pitch<D>::K + 16 * kd);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kd], s1, 0, 0, 0);
+      for (int st = 0; st < NST; ++st)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+          const int key = 32 * (kh + st) + 8 * (a >> 2) + 4 * g + (a & 3);
+          if (key >= valid) s[st][a] = -INFINITY;
+        }
     }
-    float mx = fmaxf(s0[0], s1[0]);
+    float mx = s[0][0];
+    if constexpr (NST == 2) {
 #pragma unroll
-    for (int a = 1; a < 16; ++a) mx = fmaxf(fmaxf(mx, s0[a]), s1[a]);  // v_max3
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * scale_log2;
+      for (int a = 0; a < 16; ++a) mx = fmaxf(fmaxf(mx, s[0][a]), s[1][a]);  // v_max3
+    } else {
+#pragma unroll
+      for (int a = 1; a < 16; a += 2) mx = fmaxf(fmaxf(mx, s[0][a]), s[0][a + 1 < 16 ? a + 1 : a]);
+    }
+    mx = fmaxf(mx, xchg32(mx, g)) * scale_log2;
     const bool grow = mx > m_ref + kRescaleLog2;
     if (__ballot(grow)) {
       // a real branch: keeps the compiler from turning the rare rescale into an
@@ -232,16 +270,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
         for (int a = 0; a < 16; ++a) acc_o[t][a] *= alpha;
     }
-    bf16x8 pf[4];
+    // a wave whose keys so far were all masked has m_ref = -inf: its weights are 0
+    const float m_use = KS == 1 ? m_ref : (m_ref == -INFINITY ? 0.f : m_ref);
+    bf16x8 pf[2 * NST];
 #pragma unroll
-    for (int a = 0; a < 16; ++a) {
-      pf[a >> 3][a & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s0[a], scale_log2, -m_ref));
-      pf[2 + (a >> 3)][a & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s1[a], scale_log2, -m_ref));
-    }
+    for (int st = 0; st < NST; ++st)
+#pragma unroll
+      for (int a = 0; a < 16; ++a)
+        pf[2 * st + (a >> 3)][a & 7] =
+            (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[st][a], scale_log2, -m_use));
     // row sum of the rounded weights (so the weights applied to V sum to exactly 1)
     float psum = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < 2 * NST; ++kk) {
       const bf16x2* pp = (const bf16x2*)&pf[kk];
 #pragma unroll
       for (int i = 0; i < 4; ++i) psum = __builtin_amdgcn_fdot2_f32_bf16(pp[i], ones, psum, false);
@@ -252,10 +293,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     // c = l%4) addresses key row 16kk+4g+j (+8 for the second half) at head-dim
     // columns 32t + 16*((l/16)%2) + 4c .. +3.
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < 2 * NST; ++kk) {
 #pragma unroll
       for (int t = 0; t < D / 32; ++t) {
-        const uint16_t* p0 = sv + vt_off + 16 * kk * Pitch<D>::V + 32 * t;
+        const uint16_t* p0 = sv + vt_off + 16 * (2 * kh + kk) * Pitch<D>::V + 32 * t;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (s16x4 __attribute__((address_space(3)))*)(p0));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -274,16 +315,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     TileIter nx = it;
     nx.next();
     if (nx.valid()) load(nx);
-    if (__builtin_expect(valid != bias_valid, 0)) {
-      bias_valid = valid;
-#pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        const int key = 8 * (a >> 2) + 4 * g + (a & 3);
-        bias0[a] = key < valid ? 0.f : -INFINITY;
-        bias1[a] = key + 32 < valid ? 0.f : -INFINITY;
-      }
-    }
-    tile(sm.k[buf], sm.v[buf]);
+    tile(sm.k[buf], sm.v[buf], valid);
     if (nx.valid()) store(buf ^ 1);
     __syncthreads();
     buf ^= 1;
@@ -291,6 +323,30 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   }
 
   // ---- epilogue
+  if constexpr (KS == 2) {
+    // merge the two key halves: waves 2, 3 hand (m, l, O) to waves 0, 1 through LDS
+    float* xb = (float*)&sm + (qw * kWave + l) * (2 + D / 2);
+    if (kh == 1) {
+      xb[0] = m_ref;
+      xb[1] = l_run;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) xb[2 + 16 * t + a] = acc_o[t][a];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float m1 = xb[0], l1 = xb[1];
+    const float mm = fmaxf(m_ref, m1);
+    const float a0 = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - mm);
+    const float a1 = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+    l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) acc_o[t][a] = acc_o[t][a] * a0 + xb[2 + 16 * t + a] * a1;
+    m_ref = mm;
+  }
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
   if (my_q < q_hi) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -377,23 +433,23 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
                          a.scale);
     return hipGetLastError();
   }
+  const float sl2 = a.scale * kLog2e;
+  const int ks = a.block_q <= kBM / 2 ? 2 : 1;
   Work wk;
   wk.nbq = nbq;
-  wk.mt_per_qb = (a.block_q + kBM - 1) / kBM;
+  wk.mt_per_qb = (a.block_q + kBM / ks - 1) / (kBM / ks);
   wk.items = a.batch * a.heads * (int64_t)nbq * wk.mt_per_qb;
   wk.per_xcd = (wk.items + 7) / 8;
   const dim3 grid((unsigned)(wk.per_xcd * 8));
-  const float sl2 = a.scale * kLog2e;
+  auto launch = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.nq, a.nk,
+                       a.heads, a.block_q, a.block_k, a.row_ptr, a.col_idx, a.n_slabs, sl2, wk);
+  };
   if (a.head_dim == 64)
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, dim3(kThreads), 0, stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (uint16_t*)a.o, a.lse, a.nq, a.nk, a.heads, a.block_q, a.block_k,
-                       a.row_ptr, a.col_idx, a.n_slabs, sl2, wk);
+    ks == 2 ? launch(attn_fwd_bf16_kernel<64, 2>) : launch(attn_fwd_bf16_kernel<64, 1>);
   else
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, dim3(kThreads), 0, stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (uint16_t*)a.o, a.lse, a.nq, a.nk, a.heads, a.block_q, a.block_k,
-                       a.row_ptr, a.col_idx, a.n_slabs, sl2, wk);
+    ks == 2 ? launch(attn_fwd_bf16_kernel<128, 2>) : launch(attn_fwd_bf16_kernel<128, 1>);
   return hipGetLastError();
 }
 

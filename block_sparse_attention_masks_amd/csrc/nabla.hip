@@ -59,8 +59,10 @@ __device__ inline void widen8(const uint4& u, double* out, bool bf16, const uint
   }
 }
 
-// grid: x = query blocks then key blocks, y = column slices of 8*kThreads, z = batch.
-__global__ __launch_bounds__(kThreads) void pool_kernel(const uint8_t* __restrict__ q,
+// grid: x = query blocks then key blocks, y = column slices of 8*blockDim.x elements,
+// z = batch.  The host sizes blockDim.x so that the slices cover a row evenly.
+constexpr int kPoolMaxThreads = 512;
+__global__ __launch_bounds__(kPoolMaxThreads) void pool_kernel(const uint8_t* __restrict__ q,
                                                         const uint8_t* __restrict__ k, int bf16,
                                                         int64_t nq, int64_t nk, int bq, int bk,
                                                         int nbq, int nbk, int heads, int D,
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const uint8_t* __restric
   double* dst = isq ? qp : kp;
   const int64_t b = blockIdx.z;
   const int hd = heads * D;
-  const int vec = blockIdx.y * kThreads + threadIdx.x;  // 8-element vector index in a row
+  const int vec = blockIdx.y * blockDim.x + threadIdx.x;  // 8-element vector index in a row
   if (vec * 8 >= hd) return;
   const int esz = bf16 ? 2 : 4;
   const int64_t row_bytes = (int64_t)hd * esz;
@@ -194,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
                                                           int32_t* __restrict__ row_ptr) {
   extern __shared__ double smem[];
   __shared__ double red[kThreads / kWave];
-  __shared__ double tsum[kThreads];
+  __shared__ double tsum[kThreads / kWave];
   __shared__ int cut_s;
   double* key = smem;
   int* idx = (int*)(key + SN);
@@ -263,10 +265,18 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
       const int per = SN / kThreads, i0 = t * per;
       double local = 0;
       for (int i = 0; i < per; ++i) local += (i0 + i < nbk) ? key[i0 + i] : 0.0;
-      tsum[t] = local;
+      // exclusive prefix of the per-thread totals: wave scan, then wave offsets
+      double incl = local;
+      const int ln = lane_id(), wv = t / kWave;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const double y = __shfl_up(incl, o, kWave);
+        if (ln >= o) incl += y;
+      }
+      if (ln == kWave - 1) tsum[wv] = incl;
       __syncthreads();
-      double before_sum = 0;
-      for (int u = 0; u < t; ++u) before_sum += tsum[u];
+      double before_sum = incl - local;
+      for (int u = 0; u < wv; ++u) before_sum += tsum[u];
       double c = before_sum;
       for (int i = 0; i < per; ++i) {
         if (i0 + i >= nbk) break;
@@ -344,8 +354,14 @@ hipError_t launch_mask_nabla(const NablaArgs& a, hipStream_t stream) {
   uint32_t* bitmap = (uint32_t*)(ws + L.bits);
   const int hd = a.heads * a.head_dim;
 
-  dim3 g1(nbq + nbk, (hd / 8 + kThreads - 1) / kThreads, (unsigned)a.batch);
-  hipLaunchKernelGGL(pool_kernel, g1, dim3(kThreads), 0, stream, (const uint8_t*)a.q,
+  // threads per workgroup: the row's 8-element vectors split evenly into slices of at
+  // most kPoolMaxThreads, rounded up to whole waves
+  const int vpr = hd / 8;
+  const int slices = (vpr + kPoolMaxThreads - 1) / kPoolMaxThreads;
+  const int per = (vpr + slices - 1) / slices;
+  const int pool_threads = (per + kWave - 1) / kWave * kWave;
+  dim3 g1(nbq + nbk, (vpr + pool_threads - 1) / pool_threads, (unsigned)a.batch);
+  hipLaunchKernelGGL(pool_kernel, g1, dim3(pool_threads), 0, stream, (const uint8_t*)a.q,
                      (const uint8_t*)a.k, a.dtype == 1 ? 1 : 0, a.nq, a.nk, a.block_q, a.block_k,
                      nbq, nbk, a.heads, a.head_dim, qp, kp);
   hipError_t e = hipGetLastError();
