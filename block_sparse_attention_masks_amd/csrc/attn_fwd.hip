@@ -7,9 +7,9 @@
 // (batch, head, query block); each wave owns 32 of them, held in registers as
 // the B operand of S^T = K Q^T.  The kept key blocks are walked as one stream of
 // 64-key tiles:
-//   * tile t+1 is fetched from HBM into registers (16-byte loads) while tile t is
-//     computed from LDS; the registers are then written to the other half of a
-//     double-buffered LDS stage, so each tile costs one barrier;
+//   * tile t+1 is copied from HBM straight into the other half of a
+//     double-buffered LDS stage (global_load_lds, 16 bytes per lane, no staging
+//     registers) while tile t is computed; one wait + barrier per tile;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (M = keys, N = queries, K = head
 //     dim): the accumulator gives each lane one query and 16 keys, so the row max
 //     and row sum are in-lane plus one exchange between the half-waves;
@@ -54,19 +54,6 @@ struct Work {
   int nbq, mt_per_qb;
 };
 
-// LDS row pitches (elements).  K rows shift by 4 banks (conflict-free 16-byte
-// reads of 16 consecutive rows); V rows shift by 16 banks (conflict-free
-// transposed 8-byte reads of 4 consecutive rows x 64 bytes).
-template <int D> struct Pitch;
-template <> struct Pitch<128> { static constexpr int K = 136, V = 160; };
-template <> struct Pitch<64> { static constexpr int K = 72, V = 96; };
-
-template <int D>
-struct Smem {
-  uint16_t k[2][kBN * Pitch<D>::K];
-  uint16_t v[2][kBN * Pitch<D>::V];
-};
-
 // Stream of 64-key tiles over the kept blocks of one CSR row (wave-uniform).
 struct TileIter {
   const int32_t* col;
@@ -97,6 +84,96 @@ __device__ inline float xchg32(float x, int g) {
   return __uint_as_float(g == 0 ? r[1] : r[0]);
 }
 
+// ---- LDS layout --------------------------------------------------------------------
+// K and V tiles are stored unpadded (row r of a 64-key tile at r * D elements), so a
+// direct copy writes them, and the 16-byte chunks of each row are permuted by an XOR
+// so the reads below are free of bank conflicts:
+//   * K: chunk c of row r sits at slot c ^ swz_k(r).  A K-fragment read touches 32
+//     consecutive rows at one chunk pair; D = 128 spreads 16 rows over all 16 slots,
+//     D = 64 (8 slots, two rows per 256 bytes) spreads row pairs over 8 slots.
+//   * V: chunk c of row r sits at slot c ^ swz_v(r).  A transposed read touches 4
+//     consecutive rows x 64 bytes; the shift moves each of the 4 rows to its own
+//     quarter of the banks.
+template <int D> __device__ inline int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D> __device__ inline int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
+// s_waitcnt vmcnt(N), leaving the other counters alone (gfx9 encoding: vmcnt low
+// bits [3:0] and high bits [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N> __device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// One wave copies 64 x 16 bytes from global memory to LDS: lane i's 16 bytes land at
+// lds + 16 * i (lds is wave-uniform).
+__device__ inline void load_lds16(const uint16_t* src, uint16_t* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+typedef unsigned long long u64_t;
+
+// V fragments of one 16-key group for every 32-column slice of the head dim:
+// vf[t][i] = V[key_i][32 t + lane % 32] with key_i = 4 g + i (i < 4) and 8 + 4 g + i - 4
+// (i >= 4), g = lane / 32.  The reads and their wait sit in one asm block: the compiler
+// would otherwise wait for every outstanding global->LDS copy before a transposed read.
+template <int D>
+__device__ inline void read_v_step(bf16x8 (&vf)[D / 32], uint32_t base, const int (&voff)[D / 32]);
+
+template <>
+__device__ inline void read_v_step<128>(bf16x8 (&vf)[4], uint32_t base, const int (&voff)[4]) {
+  u64_t r0, r1, r2, r3, r4, r5, r6, r7;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n"
+      "ds_read_b64_tr_b16 %1, %8 offset:2048\n"
+      "ds_read_b64_tr_b16 %2, %9\n"
+      "ds_read_b64_tr_b16 %3, %9 offset:2048\n"
+      "ds_read_b64_tr_b16 %4, %10\n"
+      "ds_read_b64_tr_b16 %5, %10 offset:2048\n"
+      "ds_read_b64_tr_b16 %6, %11\n"
+      "ds_read_b64_tr_b16 %7, %11 offset:2048\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+      : "v"(base + 2 * voff[0]), "v"(base + 2 * voff[1]), "v"(base + 2 * voff[2]),
+        "v"(base + 2 * voff[3])
+      : "memory");
+  const u64_t r[8] = {r0, r1, r2, r3, r4, r5, r6, r7};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const u64_t pr[2] = {r[2 * t], r[2 * t + 1]};
+    vf[t] = __builtin_bit_cast(bf16x8, pr);
+  }
+}
+
+template <>
+__device__ inline void read_v_step<64>(bf16x8 (&vf)[2], uint32_t base, const int (&voff)[2]) {
+  u64_t r0, r1, r2, r3;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n"
+      "ds_read_b64_tr_b16 %1, %4 offset:1024\n"
+      "ds_read_b64_tr_b16 %2, %5\n"
+      "ds_read_b64_tr_b16 %3, %5 offset:1024\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(base + 2 * voff[0]), "v"(base + 2 * voff[1])
+      : "memory");
+  const u64_t r[4] = {r0, r1, r2, r3};
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const u64_t pr[2] = {r[2 * t], r[2 * t + 1]};
+    vf[t] = __builtin_bit_cast(bf16x8, pr);
+  }
+}
+
+template <int D>
+struct Smem {
+  uint16_t k[2][kBN * D];
+  uint16_t v[2][kBN * D];
+};
+
 template <int D, int KS>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -104,17 +181,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     int64_t nq, int64_t nk, int heads, int block_q, int block_k,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int n_slabs,
     float scale_log2, Work wk) {
-  __shared__ __attribute__((aligned(16))) Smem<D> sm;
-  constexpr int kPer = kBN * D / 8 / kThreads;  // 16-byte chunks per thread per tensor
-  // KS = 1: the 4 waves own 32 query rows each and all 64 keys of every tile.
-  // KS = 2 (query blocks of <= 64 rows): waves w and w+2 own the same 32 rows and
-  // split every tile's keys in halves; their softmax states merge at the end.
-  constexpr int BM = kBM / KS;   // query rows per workgroup
-  constexpr int NST = 2 / KS;    // 32-key sub-tiles per wave per tile
+  __shared__ __attribute__((aligned(1024))) Smem<D> sm;
+  constexpr int BM = kBM / KS;
+  constexpr int NST = 2 / KS;
+  constexpr int SPR = D / 8;              // 16-byte slots per row
+  constexpr int RPC = 64 / SPR;           // rows per 1 KB wave-load
+  constexpr int CB = kBN / RPC;           // wave-loads per tensor per tile
+  constexpr int CBW = CB / kWaves;        // ... per wave
 
-  // XCD-aware mapping: workgroups are dealt round-robin to the 8 XCDs; give each
-  // XCD a contiguous range of work items so that the query tiles of one query
-  // block (which read the same K/V) share an L2.
   const int64_t bid = blockIdx.x;
   const int64_t item = (bid % 8) * wk.per_xcd + bid / 8;
   if (item >= wk.items) return;
@@ -124,64 +198,41 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   rest /= wk.nbq;
   const int h = (int)(rest % heads);
   const int64_t b = rest / heads;
-
   const int64_t q_lo = (int64_t)qb * block_q + (int64_t)mt * BM;
   const int64_t q_hi = min(min((int64_t)(qb + 1) * block_q, nq), q_lo + BM);
   if (q_lo >= q_hi) return;
 
   const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
   const int col = l & 31, g = l >> 5;
-  const int qw = KS == 1 ? w : (w & 1);   // this wave's 32-row query group
-  const int kh = KS == 1 ? 0 : (w >> 1);  // this wave's key half (KS = 2)
-  const int row_stride = heads * D;  // elements between tokens (validated < 2^31 / 64)
+  const int qw = KS == 1 ? w : (w & 1);
+  const int kh = KS == 1 ? 0 : (w >> 1);
+  const int row_stride = heads * D;
 
   const int64_t slab = n_slabs == 1 ? 0 : b * heads + h;
   const int64_t r = slab * wk.nbq + qb;
   TileIter it{col_idx, row_ptr[r], row_ptr[r + 1], 0, 0, block_k, nk};
   it.open();
-
   const uint16_t* kbase = k + (b * nk * heads + h) * (int64_t)D;
   const uint16_t* vbase = v + (b * nk * heads + h) * (int64_t)D;
 
-  // This thread stages chunks tid + 256 i of each tile: key row krow0 + kRowStep*i,
-  // head-dim columns d8 .. d8+7 (the same for every tile).
-  constexpr int kRowStep = kThreads / (D / 8);
-  const int krow0 = tid / (D / 8), d8 = (tid % (D / 8)) * 8;
-  const int goff0 = krow0 * row_stride + d8;
-  const int soff_k = krow0 * Pitch<D>::K + d8, soff_v = krow0 * Pitch<D>::V + d8;
-  u32x4 kreg[kPer], vreg[kPer];
-  auto load = [&](const TileIter& t) {
-    const uint16_t* kb = kbase + t.k0 * row_stride + goff0;
-    const uint16_t* vb = vbase + t.k0 * row_stride + goff0;
-    const int nv = (int)min((int64_t)kBN, t.ke - t.k0);
-    if (nv == kBN) {
+  int lrow[CBW], ck[CBW], cv[CBW];
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        kreg[i] = *(const u32x4*)(kb + i * kRowStep * row_stride);
-        vreg[i] = *(const u32x4*)(vb + i * kRowStep * row_stride);
-      }
-    } else {  // ragged tail: rows past the block read as zero
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const bool ok = krow0 + i * kRowStep < nv;
-        kreg[i] = ok ? *(const u32x4*)(kb + i * kRowStep * row_stride) : u32x4{0, 0, 0, 0};
-        vreg[i] = ok ? *(const u32x4*)(vb + i * kRowStep * row_stride) : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store = [&](int bufi) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      *(u32x4*)(sm.k[bufi] + soff_k + i * kRowStep * Pitch<D>::K) = kreg[i];
-      *(u32x4*)(sm.v[bufi] + soff_v + i * kRowStep * Pitch<D>::V) = vreg[i];
-    }
-  };
-  if (it.valid()) {
-    load(it);
-    store(0);
+  for (int j = 0; j < CBW; ++j) {
+    const int cb = w + kWaves * j;
+    lrow[j] = cb * RPC + l / SPR;
+    ck[j] = (l % SPR) ^ swz_k<D>(lrow[j]);
+    cv[j] = (l % SPR) ^ swz_v<D>(lrow[j]);
   }
+  auto issue = [&](int64_t k0, int64_t ke, int stage) {
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+      const int cb = w + kWaves * j;
+      const int64_t key = min(k0 + lrow[j], ke - 1);
+      load_lds16(kbase + key * row_stride + 8 * ck[j], sm.k[stage] + cb * 512);
+      load_lds16(vbase + key * row_stride + 8 * cv[j], sm.v[stage] + cb * 512);
+    }
+  };
 
-  // Q fragments (B operand of S^T = K Q^T): query col, dims 16*s + 8*g .. +7.
   const int64_t my_q = q_lo + qw * 32 + col;
   bf16x8 qf[D / 16];
   {
@@ -193,6 +244,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
       qf[s] = __builtin_bit_cast(bf16x8, u);
     }
   }
+  if (it.valid()) issue(it.k0, it.ke, 0);
 
   f32x16 acc_o[D / 32];
 #pragma unroll
@@ -201,43 +253,37 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     for (int a = 0; a < 16; ++a) acc_o[t][a] = 0.f;
   float m_ref = -INFINITY, l_run = 0.f;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  // transposed-read lane address inside a V tile: key row 4g + j, columns
-  // 16*((l/16)%2) + 4c (plus 32t and 16kk rows per product step)
-  const int vt_off = (4 * g + ((l & 15) >> 2)) * Pitch<D>::V + 16 * ((l >> 4) & 1) + 4 * (l & 3);
-  const int k_off = col * Pitch<D>::K + 8 * g;
+  const int kx = g ^ swz_k<D>(col);   // K slot of (row 32 st + col, chunk 2 kd + g) = (2 kd) ^ kx
+  const int jv = (l & 15) >> 2, c4 = l & 3, m2 = (l >> 4) & 1;
+  int voff[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+    voff[t] = (4 * g + jv) * D + 8 * (((4 * t + 2 * m2 + (c4 >> 1)) ^ swz_v<D>(4 * g + jv))) + 4 * (c4 & 1);
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
 
-  // One 64-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  `valid` < 64
-  // only for the ragged last tile of a block.
-  auto tile = [&](const uint16_t* sk, const uint16_t* sv, int valid) {
+  int buf = 0;
+  while (it.valid()) {
+    const int valid = (int)min((int64_t)kBN, it.ke - it.k0);
+    TileIter nx = it;
+    nx.next();
+    if (nx.valid()) issue(nx.k0, nx.ke, buf ^ 1);
+    const uint16_t* sk = sm.k[buf];
+    const uint16_t* sv = sm.v[buf];
     f32x16 s[NST];
 #pragma unroll
     for (int st = 0; st < NST; ++st)
 #pragma unroll
       for (int a = 0; a < 16; ++a) s[st][a] = 0.f;
-    {
-      // K fragments are read kLook steps ahead of the products that use them
-      constexpr int kSteps = D / 16, kLook = 2;
-      const uint16_t* kp = sk + k_off + 32 * kh * Pitch<D>::K;
-      bf16x8 fr[kSteps][NST];
 #pragma unroll
-      for (int kd = 0; kd < kLook; ++kd)
+    for (int kd = 0; kd < D / 16; ++kd) {
 #pragma unroll
-        for (int st = 0; st < NST; ++st)
-          fr[kd][st] = *(const bf16x8*)(kp + 32 * st * Pitch<D>::K + 16 * kd);
-#pragma unroll
-      for (int kd = 0; kd < kSteps; ++kd) {
-        if (kd + kLook < kSteps) {
-#pragma unroll
-          for (int st = 0; st < NST; ++st)
-            fr[kd + kLook][st] = *(const bf16x8*)(kp + 32 * st * Pitch<D>::K + 16 * (kd + kLook));
-        }
-#pragma unroll
-        for (int st = 0; st < NST; ++st)
-          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[kd][st], qf[kd], s[st], 0, 0, 0);
+      for (int st = 0; st < NST; ++st) {
+        const bf16x8 af = *(const bf16x8*)(sk + (32 * (kh + st) + col) * D + 8 * ((2 * kd) ^ kx));
+        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[kd], s[st], 0, 0, 0);
       }
     }
     if (valid < kBN) {
-      // a real branch (kept out of the full-tile path): keys past the tail score -inf
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int st = 0; st < NST; ++st)
@@ -250,16 +296,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     float mx = s[0][0];
     if constexpr (NST == 2) {
 #pragma unroll
-      for (int a = 0; a < 16; ++a) mx = fmaxf(fmaxf(mx, s[0][a]), s[1][a]);  // v_max3
+      for (int a = 0; a < 16; ++a) mx = fmaxf(fmaxf(mx, s[0][a]), s[1][a]);
     } else {
 #pragma unroll
-      for (int a = 1; a < 16; a += 2) mx = fmaxf(fmaxf(mx, s[0][a]), s[0][a + 1 < 16 ? a + 1 : a]);
+      for (int a = 1; a < 15; a += 2) mx = fmaxf(fmaxf(mx, s[0][a]), s[0][a + 1]);
+      mx = fmaxf(mx, s[0][15]);
     }
     mx = fmaxf(mx, xchg32(mx, g)) * scale_log2;
     const bool grow = mx > m_ref + kRescaleLog2;
     if (__ballot(grow)) {
-      // a real branch: keeps the compiler from turning the rare rescale into an
-      // unconditional multiply by a selected factor
       asm volatile("" ::: "memory");
       const float m_new = grow ? mx : m_ref;
       const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
@@ -270,7 +315,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
         for (int a = 0; a < 16; ++a) acc_o[t][a] *= alpha;
     }
-    // a wave whose keys so far were all masked has m_ref = -inf: its weights are 0
     const float m_use = KS == 1 ? m_ref : (m_ref == -INFINITY ? 0.f : m_ref);
     bf16x8 pf[2 * NST];
 #pragma unroll
@@ -279,7 +323,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
       for (int a = 0; a < 16; ++a)
         pf[2 * st + (a >> 3)][a & 7] =
             (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[st][a], scale_log2, -m_use));
-    // row sum of the rounded weights (so the weights applied to V sum to exactly 1)
     float psum = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 2 * NST; ++kk) {
@@ -288,43 +331,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
       for (int i = 0; i < 4; ++i) psum = __builtin_amdgcn_fdot2_f32_bf16(pp[i], ones, psum, false);
     }
     l_run += psum;
-
-    // O^T += V^T P^T; A operand (V^T) by transposed LDS reads: lane (j = (l%16)/4,
-    // c = l%4) addresses key row 16kk+4g+j (+8 for the second half) at head-dim
-    // columns 32t + 16*((l/16)%2) + 4c .. +3.
 #pragma unroll
     for (int kk = 0; kk < 2 * NST; ++kk) {
+      bf16x8 vf[D / 32];
+      read_v_step<D>(vf, lds_addr(sv + 16 * (2 * kh + kk) * D), voff);
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) {
-        const uint16_t* p0 = sv + vt_off + 16 * (2 * kh + kk) * Pitch<D>::V + 32 * t;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (s16x4 __attribute__((address_space(3)))*)(p0));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (s16x4 __attribute__((address_space(3)))*)(p0 + 8 * Pitch<D>::V));
-        const s16x4 vv[2] = {lo, hi};
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, vv);
-        acc_o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], acc_o[t], 0, 0, 0);
-      }
+      for (int t = 0; t < D / 32; ++t)
+        acc_o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t], pf[kk], acc_o[t], 0, 0, 0);
     }
-  };
-  __syncthreads();
-
-  int buf = 0;
-  while (it.valid()) {
-    const int valid = (int)min((int64_t)kBN, it.ke - it.k0);
-    TileIter nx = it;
-    nx.next();
-    if (nx.valid()) load(nx);
-    tile(sm.k[buf], sm.v[buf], valid);
-    if (nx.valid()) store(buf ^ 1);
-    __syncthreads();
+    wait_vmcnt<0>();               // the next tile's loads have landed
+    __builtin_amdgcn_s_barrier();  // ... for everyone; this tile is no longer read
     buf ^= 1;
     it = nx;
   }
 
   // ---- epilogue
   if constexpr (KS == 2) {
-    // merge the two key halves: waves 2, 3 hand (m, l, O) to waves 0, 1 through LDS
     float* xb = (float*)&sm + (qw * kWave + l) * (2 + D / 2);
     if (kh == 1) {
       xb[0] = m_ref;
@@ -347,7 +369,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
       for (int a = 0; a < 16; ++a) acc_o[t][a] = acc_o[t][a] * a0 + xb[2 + 16 * t + a] * a1;
     m_ref = mm;
   }
-  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+  const float l_tot = l_run + xchg32(l_run, g);
   if (my_q < q_hi) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* op = o + ((b * nq + my_q) * heads + h) * D;
