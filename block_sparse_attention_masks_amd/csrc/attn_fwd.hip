@@ -3,10 +3,13 @@
 // solution" part 3: head-wise sparse attention on the kept blocks only; the
 // pages' masks decide which blocks are kept).
 //
-// bf16 path (matrix cores).  A workgroup of 4 waves owns 128 query rows of one
-// (batch, head, query block); each wave owns 32 of them, held in registers as
-// the B operand of S^T = K Q^T.  The kept key blocks are walked as one stream of
-// 64-key tiles:
+// bf16 path (matrix cores).  A workgroup of NW waves owns 32 * NW query rows of
+// one (batch, head, query block); each wave owns 32 of them, held in registers as
+// the B operand of S^T = K Q^T.  NW is 12 or 8 when the query block is a multiple
+// of 384 or 256 rows (one copy of each K/V tile then serves that many rows; the
+// bytes copied per flop, not their latency, are what the copies cost), else 4;
+// blocks of at most 64 rows split each tile's keys between two wave pairs.  The
+// kept key blocks are walked as one stream of 64-key tiles:
 //   * tile t+1 is copied from HBM straight into the other half of a
 //     double-buffered LDS stage (global_load_lds, 16 bytes per lane, no staging
 //     registers) while tile t is computed; one wait + barrier per tile;
@@ -42,10 +45,8 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 128;      // query rows per workgroup
+constexpr int kBM = 128;      // query rows per 4-wave workgroup
 constexpr int kBN = 64;       // keys per tile
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * kWave;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale slack (exponents stay <= 2^8)
 
@@ -174,20 +175,21 @@ struct Smem {
   uint16_t v[2][kBN * D];
 };
 
-template <int D, int KS>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
+template <int D, int KS, int NW>
+__global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
     int64_t nq, int64_t nk, int heads, int block_q, int block_k,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int n_slabs,
     float scale_log2, Work wk) {
   __shared__ __attribute__((aligned(1024))) Smem<D> sm;
-  constexpr int BM = kBM / KS;
+  static_assert(KS == 1 || NW == 4, "key split runs with 4 waves");
+  constexpr int BM = 32 * NW / KS;
   constexpr int NST = 2 / KS;
   constexpr int SPR = D / 8;              // 16-byte slots per row
   constexpr int RPC = 64 / SPR;           // rows per 1 KB wave-load
   constexpr int CB = kBN / RPC;           // wave-loads per tensor per tile
-  constexpr int CBW = CB / kWaves;        // ... per wave
+  constexpr int NJ = (2 * CB + NW - 1) / NW;  // wave-loads per wave per tile (K and V together)
 
   const int64_t bid = blockIdx.x;
   const int64_t item = (bid % 8) * wk.per_xcd + bid / 8;
@@ -202,7 +204,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const int64_t q_hi = min(min((int64_t)(qb + 1) * block_q, nq), q_lo + BM);
   if (q_lo >= q_hi) return;
 
-  const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
+  const int tid = threadIdx.x, l = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int col = l & 31, g = l >> 5;
   const int qw = KS == 1 ? w : (w & 1);
   const int kh = KS == 1 ? 0 : (w >> 1);
@@ -215,21 +218,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const uint16_t* kbase = k + (b * nk * heads + h) * (int64_t)D;
   const uint16_t* vbase = v + (b * nk * heads + h) * (int64_t)D;
 
-  int lrow[CBW], ck[CBW], cv[CBW];
+  // Copy plan: wave-load c = w + NW j (c < 2 CB) moves RPC rows of K (c < CB) or of V
+  // (chunk-block c - CB) of the tile; the tile base is wave-uniform, each lane adds a
+  // loop-invariant row and chunk.  Rows past the last key repeat it (masked later).
+  const uint32_t row_bytes = 2u * (uint32_t)row_stride;
+  int lrow[NJ];
+  uint32_t ch16[NJ];
 #pragma unroll
-  for (int j = 0; j < CBW; ++j) {
-    const int cb = w + kWaves * j;
+  for (int j = 0; j < NJ; ++j) {
+    const int c = w + NW * j;
+    const int cb = c < CB ? c : c - CB;
     lrow[j] = cb * RPC + l / SPR;
-    ck[j] = (l % SPR) ^ swz_k<D>(lrow[j]);
-    cv[j] = (l % SPR) ^ swz_v<D>(lrow[j]);
+    ch16[j] = 16u * ((l % SPR) ^ (c < CB ? swz_k<D>(lrow[j]) : swz_v<D>(lrow[j])));
   }
   auto issue = [&](int64_t k0, int64_t ke, int stage) {
+    const char* kt = (const char*)(kbase + k0 * row_stride);
+    const char* vt = (const char*)(vbase + k0 * row_stride);
+    const int last = (int)min(ke - k0, (int64_t)kBN) - 1;
 #pragma unroll
-    for (int j = 0; j < CBW; ++j) {
-      const int cb = w + kWaves * j;
-      const int64_t key = min(k0 + lrow[j], ke - 1);
-      load_lds16(kbase + key * row_stride + 8 * ck[j], sm.k[stage] + cb * 512);
-      load_lds16(vbase + key * row_stride + 8 * cv[j], sm.v[stage] + cb * 512);
+    for (int j = 0; j < NJ; ++j) {
+      const int c = w + NW * j;
+      if (c < 2 * CB) {
+        const uint32_t ro = __umul24((uint32_t)min(lrow[j], last), row_bytes) + ch16[j];
+        if (c < CB)
+          load_lds16((const uint16_t*)(kt + ro), sm.k[stage] + c * 512);
+        else
+          load_lds16((const uint16_t*)(vt + ro), sm.v[stage] + (c - CB) * 512);
+      }
     }
   };
 
@@ -275,23 +290,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     for (int st = 0; st < NST; ++st)
 #pragma unroll
       for (int a = 0; a < 16; ++a) s[st][a] = 0.f;
+    bf16x8 kf[D / 16][NST];  // the whole K tile of this wave, read before the first product
 #pragma unroll
-    for (int kd = 0; kd < D / 16; ++kd) {
+    for (int kd = 0; kd < D / 16; ++kd)
 #pragma unroll
-      for (int st = 0; st < NST; ++st) {
-        const bf16x8 af = *(const bf16x8*)(sk + (32 * (kh + st) + col) * D + 8 * ((2 * kd) ^ kx));
-        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[kd], s[st], 0, 0, 0);
-      }
-    }
+      for (int st = 0; st < NST; ++st)
+        kf[kd][st] = *(const bf16x8*)(sk + (32 * (kh + st) + col) * D + 8 * ((2 * kd) ^ kx));
+#pragma unroll
+    for (int kd = 0; kd < D / 16; ++kd)
+#pragma unroll
+      for (int st = 0; st < NST; ++st)
+        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kd][st], qf[kd], s[st], 0, 0, 0);
     if (valid < kBN) {
       asm volatile("" ::: "memory");
+      const int lim = valid - 4 * g - 32 * kh;  // key index minus its lane part
 #pragma unroll
       for (int st = 0; st < NST; ++st)
 #pragma unroll
-        for (int a = 0; a < 16; ++a) {
-          const int key = 32 * (kh + st) + 8 * (a >> 2) + 4 * g + (a & 3);
-          if (key >= valid) s[st][a] = -INFINITY;
-        }
+        for (int a = 0; a < 16; ++a)
+          if (32 * st + 8 * (a >> 2) + (a & 3) >= lim) s[st][a] = -INFINITY;
     }
     float mx = s[0][0];
     if constexpr (NST == 2) {
@@ -456,22 +473,34 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const float sl2 = a.scale * kLog2e;
+  // Query rows per workgroup: 64 (key split) for small blocks; else 32 rows per wave with
+  // 12 or 8 waves when the block is a multiple of 384 or 256 rows (one K/V tile copy then
+  // serves more rows), else 4 waves.
   const int ks = a.block_q <= kBM / 2 ? 2 : 1;
+  const int nw = ks == 2 ? 4 : (a.block_q % 384 == 0 ? 12 : (a.block_q % 256 == 0 ? 8 : 4));
+  const int bm = 32 * nw / ks;
   Work wk;
   wk.nbq = nbq;
-  wk.mt_per_qb = (a.block_q + kBM / ks - 1) / (kBM / ks);
+  wk.mt_per_qb = (a.block_q + bm - 1) / bm;
   wk.items = a.batch * a.heads * (int64_t)nbq * wk.mt_per_qb;
   wk.per_xcd = (wk.items + 7) / 8;
   const dim3 grid((unsigned)(wk.per_xcd * 8));
   auto launch = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, (const uint16_t*)a.q,
+    hipLaunchKernelGGL(kern, grid, dim3(nw * kWave), 0, stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.nq, a.nk,
                        a.heads, a.block_q, a.block_k, a.row_ptr, a.col_idx, a.n_slabs, sl2, wk);
   };
-  if (a.head_dim == 64)
-    ks == 2 ? launch(attn_fwd_bf16_kernel<64, 2>) : launch(attn_fwd_bf16_kernel<64, 1>);
-  else
-    ks == 2 ? launch(attn_fwd_bf16_kernel<128, 2>) : launch(attn_fwd_bf16_kernel<128, 1>);
+  if (a.head_dim == 64) {
+    if (ks == 2) launch(attn_fwd_bf16_kernel<64, 2, 4>);
+    else if (nw == 12) launch(attn_fwd_bf16_kernel<64, 1, 12>);
+    else if (nw == 8) launch(attn_fwd_bf16_kernel<64, 1, 8>);
+    else launch(attn_fwd_bf16_kernel<64, 1, 4>);
+  } else {
+    if (ks == 2) launch(attn_fwd_bf16_kernel<128, 2, 4>);
+    else if (nw == 12) launch(attn_fwd_bf16_kernel<128, 1, 12>);
+    else if (nw == 8) launch(attn_fwd_bf16_kernel<128, 1, 8>);
+    else launch(attn_fwd_bf16_kernel<128, 1, 4>);
+  }
   return hipGetLastError();
 }
 

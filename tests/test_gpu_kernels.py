@@ -128,6 +128,8 @@ CASES = [
     (500, 900, 2, 64, 100, 70, 0.5, 2, torch.bfloat16),          # blocks not multiples of 64
     (130, 4100, 1, 128, 64, 64, 0.2, 1, torch.bfloat16),         # nq != nk, long keys
     (300, 300, 2, 128, 300, 1, 0.3, 2, torch.bfloat16),          # one-token key blocks
+    (1100, 800, 2, 128, 256, 128, 0.5, 2, torch.bfloat16),       # 8-wave workgroups, ragged
+    (1600, 1500, 1, 64, 768, 256, 0.7, 1, torch.bfloat16),       # 12-wave, two per block
     (2048, 2048, 2, 64, 64, 64, 0.5, 2, torch.float32),
     (200, 333, 2, 128, 32, 48, 0.5, 1, torch.float32),
 ]
