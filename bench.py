@@ -66,6 +66,14 @@ def attn_flops(rp, ci, block_q, block_k, nq, nk, D, bh, n_slabs):
     return 4.0 * D * total * (bh if n_slabs == 1 else 1)
 
 
+def attn_kernel_name(D, block_q):
+    """The bf16 instantiation the library launches for this block size (the library picks
+    4-wave key-split, 12-, 8- or 4-wave workgroups from block_q)."""
+    ks = 2 if block_q <= 64 else 1
+    nw = 4 if ks == 2 else (12 if block_q % 384 == 0 else (8 if block_q % 256 == 0 else 4))
+    return f"attn_fwd_bf16_kernel<{D}, {ks}, {nw}>"
+
+
 def source_hash(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -285,7 +293,7 @@ def main():
                    "parallelism": "none (one GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": f"attn_fwd_bf16_kernel<{path.D}>",
+                     "traffic": traffic, "kernel": attn_kernel_name(path.D, path.bq),
                      "flops_per_launch": flops, "ms_per_launch": round(attn_ms, 4)},
         "cpu_baseline": cpu,
         "attn_tflops": round(attn_tflops, 2),
