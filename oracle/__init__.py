@@ -17,6 +17,9 @@ from the pages, step by step, in fp64 (numpy):
                             aibr.jp/archives/124678, sec. 1 and 3)
   masks.mask_ar          -- anchors + recent + selected blocks (Sparse Forcing
                             summary, gist.science/ja/paper/2604.21221, part 2)
+  masks.mask_sta_heads   -- STA with a window per head (STA explainer, sec. 1)
+  masks.mask_union       -- union of two masks, e.g. NABLA with STA (NABLA
+                            explainer, sec. 2 and 4)
   attention.attention    -- exact softmax(Q K^T * scale) V over the kept blocks
 
 Where the pages leave a step open, the reading taken is stated in the function.
@@ -25,5 +28,6 @@ from .reorder import tile_reorder, tile_order_source  # noqa: F401
 from .masks import (  # noqa: F401
     csr_from_bool, csr_to_bool, mask_all, mask_sta, mask_radial, radial_keep_tokens,
     pool_blocks, nabla_select_row, mask_nabla, ar_forced_ranges, ar_select_row, mask_ar,
+    mask_sta_heads, mask_union, csr_concat,
 )
 from .attention import attention, attention_rows, block_softmax  # noqa: F401

@@ -63,6 +63,56 @@ def mask_sta(grid, tile, window):
     return csr_from_bool(keep)
 
 
+def mask_sta_heads(grid, tile, windows, batch=1):
+    """STA with one window per head: slab b * heads + h uses windows[h].
+
+    Sliding Tile Attention explainer (aibr.jp/archives/60739), sec. 1: besides 3D
+    locality, attention heads specialise, so a window sized per head is the plain
+    extension of the shared window of mask_sta.  The slabs are stacked in
+    (batch, head) order, the CSR convention of the per-head masks.
+    """
+    parts = [mask_sta(grid, tile, windows[h]) for h in range(len(windows))]
+    rows = [parts[h] for _ in range(batch) for h in range(len(windows))]
+    return csr_concat(rows)
+
+
+def csr_concat(parts):
+    """Stack CSR masks (row_ptr, col_idx) vertically."""
+    row_ptr, cols, off = [0], [], 0
+    for rp, ci in parts:
+        row_ptr.extend((np.asarray(rp[1:], np.int64) + off).tolist())
+        cols.append(np.asarray(ci, np.int64))
+        off += int(rp[-1])
+    return (np.asarray(row_ptr, np.int32),
+            np.concatenate(cols).astype(np.int32) if cols else np.zeros(0, np.int32))
+
+
+def mask_union(rp_a, ci_a, slabs_a, rp_b, ci_b, slabs_b, n_qblocks):
+    """Row-by-row union of two block masks.
+
+    NABLA explainer (aibr.jp/archives/124678), sec. 2 and 4: the NABLA mask works
+    alongside other accelerations and the two combine; reading taken: a combined
+    mask keeps a block pair iff either mask keeps it (e.g. NABLA with an STA
+    window).  A mask with one slab is shared by every (batch, head) slab of the
+    other; the result has max(slabs_a, slabs_b) slabs.
+    """
+    slabs = max(slabs_a, slabs_b)
+    if slabs_a not in (1, slabs) or slabs_b not in (1, slabs):
+        raise ValueError("slab counts must be equal or 1")
+    rows = []
+    for s in range(slabs):
+        sa, sb = (s if slabs_a > 1 else 0), (s if slabs_b > 1 else 0)
+        for i in range(n_qblocks):
+            ra, rb = sa * n_qblocks + i, sb * n_qblocks + i
+            a = set(ci_a[rp_a[ra]:rp_a[ra + 1]].tolist())
+            b = set(ci_b[rp_b[rb]:rp_b[rb + 1]].tolist())
+            rows.append(sorted(a | b))
+    row_ptr = np.zeros(len(rows) + 1, np.int64)
+    row_ptr[1:] = np.cumsum([len(r) for r in rows])
+    col_idx = np.asarray([c for r in rows for c in r], np.int64)
+    return row_ptr.astype(np.int32), col_idx.astype(np.int32)
+
+
 # -------------------------------------------------------------------------- radial
 def radial_keep_tokens(fq, sq, fk, sk, S):
     """Token-level radial rule (broadcasts over arrays).

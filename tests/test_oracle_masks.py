@@ -290,3 +290,72 @@ def test_ar_forced_ranges_and_counts():
         row = 74 + i
         assert sorted(set(ci[rp[row]:rp[row + 1]].tolist()) - set(range(25)) - set(range(438, 512))) \
             == sorted(ranked)
+
+
+# --------------------------------------------------------------- composition
+def random_csr(rng, n_rows, n_cols, dens):
+    keep = rng.random((n_rows, n_cols)) < dens
+    return oracle.csr_from_bool(keep), keep
+
+
+@pytest.mark.parametrize("slabs_a,slabs_b", [(1, 1), (3, 3), (1, 3), (3, 1)])
+def test_union_matches_boolean_or(slabs_a, slabs_b):
+    """Union = elementwise OR of the dense boolean masks, with a one-slab mask shared."""
+    rng = np.random.default_rng(7)
+    nq, nk = 9, 13
+    (rpa, cia), ka = random_csr(rng, slabs_a * nq, nk, 0.3)
+    (rpb, cib), kb = random_csr(rng, slabs_b * nq, nk, 0.4)
+    rp, ci = oracle.mask_union(rpa, cia, slabs_a, rpb, cib, slabs_b, nq)
+    slabs = max(slabs_a, slabs_b)
+    ka = np.tile(ka, (slabs // slabs_a, 1))
+    kb = np.tile(kb, (slabs // slabs_b, 1))
+    assert np.array_equal(oracle.csr_to_bool(rp, ci, nk), ka | kb)
+    assert all(np.all(np.diff(r) > 0) for r in rows_of(rp, ci))   # strictly ascending
+
+
+def test_union_identities():
+    rng = np.random.default_rng(8)
+    (rp, ci), keep = random_csr(rng, 12, 20, 0.35)
+    empty = oracle.csr_from_bool(np.zeros((12, 20), bool))
+    full = oracle.mask_all(12, 20)
+    same = oracle.mask_union(rp, ci, 1, rp, ci, 1, 12)
+    assert np.array_equal(same[0], rp) and np.array_equal(same[1], ci)
+    e = oracle.mask_union(rp, ci, 1, *empty, 1, 12)
+    assert np.array_equal(e[0], rp) and np.array_equal(e[1], ci)
+    f = oracle.mask_union(rp, ci, 1, *full, 1, 12)
+    assert np.array_equal(f[0], full[0]) and np.array_equal(f[1], full[1])
+    (rp2, ci2), k2 = random_csr(rng, 12, 20, 0.5)
+    ab = oracle.mask_union(rp, ci, 1, rp2, ci2, 1, 12)
+    ba = oracle.mask_union(rp2, ci2, 1, rp, ci, 1, 12)
+    assert np.array_equal(ab[0], ba[0]) and np.array_equal(ab[1], ba[1])
+    # inclusion-exclusion on the counts
+    assert ab[0][-1] == keep.sum() + k2.sum() - (keep & k2).sum()
+
+
+def test_union_rejects_mismatched_slabs():
+    rp, ci = oracle.mask_all(2, 3)
+    rp2, ci2 = oracle.csr_concat([(rp, ci)] * 2)
+    rp3, ci3 = oracle.csr_concat([(rp, ci)] * 3)
+    with pytest.raises(ValueError):
+        oracle.mask_union(rp2, ci2, 2, rp3, ci3, 3, 2)
+
+
+def test_sta_heads_per_head_counts_and_order():
+    """Each slab equals the shared-window mask of its head; counts follow the closed form."""
+    grid, tile = (8, 16, 16), (4, 4, 4)
+    windows = [(1, 3, 3), (3, 1, 1), (1, 1, 1), (3, 3, 3)]
+    rp, ci = oracle.mask_sta_heads(grid, tile, windows, batch=2)
+    n = (8 // 4) * (16 // 4) * (16 // 4)
+    assert len(rp) == 2 * len(windows) * n + 1
+    for b in range(2):
+        for h, win in enumerate(windows):
+            s = b * len(windows) + h
+            ref_rp, ref_ci = oracle.mask_sta(grid, tile, win)
+            lo, hi = rp[s * n], rp[(s + 1) * n]
+            assert hi - lo == sta_closed_form_nnz(grid, tile, win)
+            assert np.array_equal(rp[s * n:(s + 1) * n + 1] - lo, ref_rp)
+            assert np.array_equal(ci[lo:hi], ref_ci)
+    # a 1x1x1 window keeps only the diagonal
+    s = 2
+    lo = rp[s * n]
+    assert np.array_equal(ci[lo:lo + n], np.arange(n))
