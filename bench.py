@@ -47,6 +47,10 @@ DESCRIPTION = {
              "(64-token blocks), pooled-map CDF threshold 0.8, per-head masks",
     "radial": "radial: 1 x 24 heads x 450,000 tokens (125x45x80 grid, 3,600 per frame), head_dim 128, "
               "bf16, raster 128-token blocks, radial energy-decay mask",
+    "nabla_sta": "nabla_sta: the nabla workload with its per-head NABLA masks united with a 3x3x5 STA "
+                 "window on the 16x6x10 tile grid",
+    "sta_heads": "sta_heads: the sta workload with one tile window per head (3x3x5, 1x3x3, 3x5x7 cycling "
+                 "over the 24 heads)",
     "ar": "ar: 1 x 12 heads, 4,680 query tokens (3x30x52 chunk) over a 32,760-token KV cache "
           "(21x30x52), head_dim 128, bf16, 64-token blocks, anchors + last 3 frames + top-16",
 }
@@ -121,7 +125,7 @@ class Path:
         self.nq, self.nk = self.q.shape[1], self.k.shape[1]
         self.scale = D ** -0.5
         self.tiled = None
-        if name in ("sta", "nabla"):
+        if name in ("sta", "nabla", "nabla_sta", "sta_heads"):
             self.tiled = (cfg["grid"], cfg["tile"])
             t = cfg["tile"]
             self.bq = self.bk = t[0] * t[1] * t[2]
@@ -141,6 +145,11 @@ class Path:
             cap = vsa.sta_capacity(cfg["grid"], cfg["tile"], cfg["window"])
             self.mask = lambda: vsa.vsa_mask_sta(cfg["grid"], cfg["tile"], cfg["window"], dev,
                                                  row_ptr=self.rp, col_idx=self.ci)
+        elif name == "sta_heads":
+            wins = [cfg["windows"][h % len(cfg["windows"])] for h in range(H)]
+            cap = vsa.sta_heads_capacity(cfg["grid"], cfg["tile"], wins, B)
+            self.mask = lambda: vsa.vsa_mask_sta_heads(cfg["grid"], cfg["tile"], wins, dev, batch=B,
+                                                       row_ptr=self.rp, col_idx=self.ci)
         elif name == "radial":
             T, Hg, Wg = cfg["grid"]
             cap = nbq * nbk
@@ -148,7 +157,7 @@ class Path:
                                                     col_idx=self.ci)
         else:
             cap = rows * nbk
-            if name == "nabla":
+            if name in ("nabla", "nabla_sta"):
                 sel = dict(threshold=cfg["threshold"])
             else:
                 T, Hg, Wg = cfg["grid"]
@@ -159,9 +168,22 @@ class Path:
                                                        sel.get("threshold", 1.0), sel.get("topk", 0),
                                                        sel.get("forced", ())),
                              dtype=torch.uint8, device=dev)
-            self.mask = lambda: vsa.vsa_mask_nabla(self.qa, self.ka, self.bq, self.bk, self.scale,
-                                                   workspace=ws, row_ptr=self.rp, col_idx=self.ci,
-                                                   **sel)
+            if name == "nabla_sta":
+                # NABLA into scratch CSR buffers, then the union with the shared STA window
+                self.rp_n = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+                self.ci_n = torch.empty(rows * nbk, dtype=torch.int32, device=dev)
+                rp_s, ci_s = vsa.vsa_mask_sta(cfg["grid"], cfg["tile"], cfg["window"], dev)
+
+                def mask():
+                    vsa.vsa_mask_nabla(self.qa, self.ka, self.bq, self.bk, self.scale, workspace=ws,
+                                       row_ptr=self.rp_n, col_idx=self.ci_n, **sel)
+                    vsa.vsa_mask_union(self.rp_n, self.ci_n, B * H, rp_s, ci_s, 1, nbq, nbk,
+                                       row_ptr=self.rp, col_idx=self.ci)
+                self.mask = mask
+            else:
+                self.mask = lambda: vsa.vsa_mask_nabla(self.qa, self.ka, self.bq, self.bk, self.scale,
+                                                       workspace=ws, row_ptr=self.rp, col_idx=self.ci,
+                                                       **sel)
         self.ci = torch.empty(cap, dtype=torch.int32, device=dev)
 
     def reorder_in(self):

@@ -35,6 +35,8 @@ _SIGS = {
     "vsa_tile_reorder": ([_P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I64, _I32, _P], _I32),
     "vsa_mask_sta": ([_I32] * 9 + [_P, _P, _I64, _P], _I32),
     "vsa_mask_radial": ([_I32, _I32, _I32, _P, _P, _I64, _P], _I32),
+    "vsa_mask_sta_heads": ([_I32] * 6 + [_P, _I32, _I64, _P, _P, _I64, _P], _I32),
+    "vsa_mask_union": ([_I64, _I32, _P, _P, _I64, _P, _P, _I64, _P, _P, _I64, _P], _I32),
     "vsa_mask_nabla": ([_P, _P, _I32, _I64, _I32, _I32, _I64, _I64, _I32, _I32, _F64,
                         ctypes.POINTER(Select), _P, _P, _I64, _P, ctypes.POINTER(ctypes.c_size_t), _P], _I32),
     "vsa_block_sparse_attn_fwd": ([_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I64, _I64, _I32, _I32,
@@ -139,6 +141,57 @@ def vsa_mask_radial(T, S, block, device, row_ptr=None, col_idx=None):
         raise ValueError("row_ptr must be int32 [n_blocks + 1] and col_idx int32")
     _check(lib().vsa_mask_radial(T, S, block, _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
                                  _stream(row_ptr)), "vsa_mask_radial")
+    return row_ptr, col_idx
+
+
+def sta_heads_capacity(grid, tile, windows, batch=1):
+    return batch * sum(sta_capacity(grid, tile, w) for w in windows)
+
+
+def vsa_mask_sta_heads(grid, tile, windows, device, batch=1, row_ptr=None, col_idx=None):
+    """STA mask with one window per head -> (row_ptr, col_idx) over batch * heads slabs
+    (slab = b * heads + h); col_idx is allocated at the capacity the call requires."""
+    heads = len(windows)
+    n = (grid[0] // tile[0]) * (grid[1] // tile[1]) * (grid[2] // tile[2])
+    cap = sta_heads_capacity(grid, tile, windows, batch)
+    if row_ptr is None:
+        row_ptr = torch.empty(batch * heads * n + 1, dtype=torch.int32, device=device)
+    if col_idx is None:
+        col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=device)
+    _require(row_ptr, "row_ptr")
+    _require(col_idx, "col_idx", row_ptr.device)
+    if row_ptr.numel() != batch * heads * n + 1 or row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise ValueError("row_ptr must be int32 [batch * heads * n_tiles + 1] and col_idx int32")
+    flat = [int(x) for w in windows for x in w]
+    arr = (ctypes.c_int32 * max(1, len(flat)))(*flat)
+    _check(lib().vsa_mask_sta_heads(*grid, *tile, ctypes.cast(arr, ctypes.c_void_p), heads, batch,
+                                    _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), _stream(row_ptr)),
+           "vsa_mask_sta_heads")
+    return row_ptr, col_idx
+
+
+def vsa_mask_union(rp_a, ci_a, slabs_a, rp_b, ci_b, slabs_b, n_qblocks, n_kblocks, row_ptr=None, col_idx=None):
+    """Row-by-row union of two CSR masks (a one-slab mask is shared) -> (row_ptr, col_idx);
+    col_idx is allocated at max(slabs) * n_qblocks * n_kblocks entries."""
+    for t, nm in ((rp_a, "rp_a"), (ci_a, "ci_a"), (rp_b, "rp_b"), (ci_b, "ci_b")):
+        _require(t, nm, rp_a.device)
+        if t.dtype != torch.int32:
+            raise ValueError(f"{nm} must be int32")
+    slabs = max(slabs_a, slabs_b)
+    rows = slabs * n_qblocks
+    if row_ptr is None:
+        row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=rp_a.device)
+    if col_idx is None:
+        col_idx = torch.empty(max(1, rows * n_kblocks), dtype=torch.int32, device=rp_a.device)
+    _require(row_ptr, "row_ptr", rp_a.device)
+    _require(col_idx, "col_idx", rp_a.device)
+    if rp_a.numel() != slabs_a * n_qblocks + 1 or rp_b.numel() != slabs_b * n_qblocks + 1:
+        raise ValueError("row_ptr inputs must hold slabs * n_qblocks + 1 entries")
+    if row_ptr.numel() != rows + 1 or row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise ValueError("row_ptr must be int32 [max(slabs) * n_qblocks + 1] and col_idx int32")
+    _check(lib().vsa_mask_union(n_qblocks, n_kblocks, _ptr(rp_a), _ptr(ci_a), slabs_a, _ptr(rp_b), _ptr(ci_b),
+                                slabs_b, _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), _stream(row_ptr)),
+           "vsa_mask_union")
     return row_ptr, col_idx
 
 

@@ -92,6 +92,53 @@ vsa_status vsa_mask_radial(int32_t T, int32_t S, int32_t block, int32_t* row_ptr
   return from_hip(vsa::launch_mask_radial(T, S, block, row_ptr, col_idx, stream));
 }
 
+vsa_status vsa_mask_sta_heads(int32_t T, int32_t H, int32_t W, int32_t tt, int32_t th, int32_t tw,
+                              const int32_t* windows, int32_t heads, int64_t batch, int32_t* row_ptr,
+                              int32_t* col_idx, int64_t col_capacity, hipStream_t stream) {
+  if (!windows || !row_ptr || !col_idx) return VSA_ERR_NULL;
+  if (T <= 0 || H <= 0 || W <= 0 || tt <= 0 || th <= 0 || tw <= 0 || heads <= 0 || batch <= 0)
+    return VSA_ERR_SHAPE;
+  if (T % tt || H % th || W % tw) return VSA_ERR_SHAPE;
+  if (heads > vsa::kMaxStaHeads) return VSA_ERR_UNSUPPORTED;
+  const int64_t NT = T / tt, NH = H / th, NW = W / tw, n = NT * NH * NW;
+  if (n > kI32Max || batch * heads * n > kI32Max) return VSA_ERR_SHAPE;
+  vsa::StaHeads p{};
+  p.NT = (int)NT, p.NH = (int)NH, p.NW = (int)NW, p.heads = heads;
+  const int64_t axis[3] = {NT, NH, NW};
+  int64_t per_batch = 0;
+  for (int h = 0; h < heads; ++h) {
+    int64_t vol = n;
+    for (int d = 0; d < 3; ++d) {
+      const int32_t w = windows[3 * h + d];
+      if (w <= 0 || w % 2 == 0) return VSA_ERR_PARAM;
+      // a half-width past the axis length keeps the whole axis, as the clipped window does
+      p.half[h][d] = (int16_t)std::min<int64_t>(w / 2, axis[d]);
+      vol *= std::min<int64_t>(w, axis[d]);
+    }
+    per_batch += vol;
+  }
+  const int64_t bound = batch * per_batch;
+  if (bound > kI32Max) return VSA_ERR_SHAPE;
+  if (col_capacity < bound) return VSA_ERR_CAPACITY;
+  return from_hip(vsa::launch_mask_sta_heads(p, batch * heads * n, row_ptr, col_idx, stream));
+}
+
+vsa_status vsa_mask_union(int64_t n_qblocks, int32_t n_kblocks, const int32_t* row_ptr_a,
+                          const int32_t* col_idx_a, int64_t slabs_a, const int32_t* row_ptr_b,
+                          const int32_t* col_idx_b, int64_t slabs_b, int32_t* row_ptr,
+                          int32_t* col_idx, int64_t col_capacity, hipStream_t stream) {
+  if (!row_ptr_a || !col_idx_a || !row_ptr_b || !col_idx_b || !row_ptr || !col_idx) return VSA_ERR_NULL;
+  if (n_qblocks <= 0 || n_kblocks <= 0 || slabs_a <= 0 || slabs_b <= 0) return VSA_ERR_SHAPE;
+  const int64_t slabs = std::max(slabs_a, slabs_b);
+  if ((slabs_a != 1 && slabs_a != slabs) || (slabs_b != 1 && slabs_b != slabs)) return VSA_ERR_PARAM;
+  if (slabs > kI32Max / n_qblocks) return VSA_ERR_SHAPE;
+  const int64_t rows = slabs * n_qblocks;
+  if (rows * n_kblocks > kI32Max) return VSA_ERR_SHAPE;
+  if (col_capacity < rows * n_kblocks) return VSA_ERR_CAPACITY;
+  const vsa::UnionArgs u{row_ptr_a, col_idx_a, row_ptr_b, col_idx_b, slabs_a, slabs_b, n_qblocks};
+  return from_hip(vsa::launch_mask_union(u, rows, row_ptr, col_idx, stream));
+}
+
 vsa_status vsa_mask_nabla(const void* q, const void* k, int32_t dtype, int64_t batch,
                           int32_t heads, int32_t head_dim, int64_t nq, int64_t nk,
                           int32_t block_q, int32_t block_k, double scale, const vsa_select* sel,

@@ -41,6 +41,23 @@ hipError_t launch_mask_radial(int T, int S, int block, int32_t* row_ptr, int32_t
 // In-place: row_ptr[1..n] holds per-row counts on entry, absolute offsets on exit.
 hipError_t launch_counts_to_offsets(int32_t* row_ptr, int64_t n_rows, hipStream_t stream);
 
+// STA with one window per head: half-widths per head, slabs in (batch, head) order.
+constexpr int kMaxStaHeads = 256;
+struct StaHeads {
+  int NT, NH, NW, heads;
+  int16_t half[kMaxStaHeads][3];
+};
+hipError_t launch_mask_sta_heads(const StaHeads& p, int64_t n_rows, int32_t* row_ptr, int32_t* col_idx,
+                                 hipStream_t stream);
+
+// Union of two CSR masks over n_qblocks rows per slab; a one-slab mask is shared.
+struct UnionArgs {
+  const int32_t *rp_a, *ci_a, *rp_b, *ci_b;
+  int64_t slabs_a, slabs_b, n_qblocks;
+};
+hipError_t launch_mask_union(const UnionArgs& u, int64_t n_rows, int32_t* row_ptr, int32_t* col_idx,
+                             hipStream_t stream);
+
 struct NablaArgs {
   const void* q;
   const void* k;

@@ -3,7 +3,8 @@
  * for AMD Instinct MI355X (gfx950).  C ABI; plain pointers and sizes.
  *
  * The path: make 3D tiles contiguous (vsa_tile_reorder), build a block mask as a
- * CSR list of kept key blocks (vsa_mask_sta, vsa_mask_radial, vsa_mask_nabla),
+ * CSR list of kept key blocks (vsa_mask_sta, vsa_mask_radial, vsa_mask_nabla; composed
+ * with vsa_mask_sta_heads and vsa_mask_union),
  * then compute exact softmax(Q K^T * scale) V over the kept blocks only
  * (vsa_block_sparse_attn_fwd).
  *
@@ -118,6 +119,51 @@ vsa_status vsa_mask_sta(int32_t T, int32_t H, int32_t W, int32_t tt, int32_t th,
 vsa_status vsa_mask_radial(int32_t T, int32_t S, int32_t block,
                            int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
                            hipStream_t stream);
+
+/*
+ * vsa_mask_sta_heads -- sliding 3D tile window with one window per head.
+ *
+ * Sliding Tile Attention explainer (aibr.jp/archives/60739), sec. 1: attention
+ * heads specialise, so each head may use its own window; every slab is the
+ * vsa_mask_sta mask of its head's window.  Slab s = b * heads + h (the per-head
+ * slab order of vsa_block_sparse_attn_fwd), row r = s * n_tiles + tile.
+ *
+ * windows   host, heads * 3 ints (wt, wh, ww) per head, odd and positive.
+ * heads     1 .. 256;  batch >= 1 (the heads' slabs repeat per batch entry).
+ * row_ptr   device, batch * heads * n_tiles + 1 ints;  col_idx  device.
+ * col_capacity must be >= batch * sum over heads of
+ *   n_tiles * min(wt, NT) * min(wh, NH) * min(ww, NW).
+ * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE, VSA_ERR_PARAM (even or non-positive
+ * window), VSA_ERR_UNSUPPORTED (more than 256 heads), VSA_ERR_CAPACITY,
+ * VSA_ERR_HIP.
+ */
+vsa_status vsa_mask_sta_heads(int32_t T, int32_t H, int32_t W, int32_t tt, int32_t th, int32_t tw,
+                              const int32_t* windows, int32_t heads, int64_t batch,
+                              int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                              hipStream_t stream);
+
+/*
+ * vsa_mask_union -- row-by-row union of two block masks (e.g. NABLA with STA).
+ *
+ * NABLA explainer (aibr.jp/archives/124678), sec. 2 and 4: the NABLA mask works
+ * alongside other accelerations and combines with them.  Output row r keeps key
+ * block j iff row r of mask A or of mask B keeps it, in ascending order.  Masks
+ * have n_qblocks rows per slab; a mask with one slab is shared by every slab of
+ * the other, and the output has max(slabs_a, slabs_b) slabs.
+ *
+ * row_ptr_a/col_idx_a, row_ptr_b/col_idx_b  device CSR inputs; every row strictly
+ *           ascending with values in [0, n_kblocks) (as the mask calls write
+ *           them); the output is undefined otherwise.
+ * row_ptr   device, max(slabs) * n_qblocks + 1 ints;  col_idx  device.
+ * col_capacity must be >= max(slabs) * n_qblocks * n_kblocks.
+ * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE, VSA_ERR_PARAM (slab counts neither equal
+ * nor 1), VSA_ERR_CAPACITY, VSA_ERR_HIP.
+ */
+vsa_status vsa_mask_union(int64_t n_qblocks, int32_t n_kblocks,
+                          const int32_t* row_ptr_a, const int32_t* col_idx_a, int64_t slabs_a,
+                          const int32_t* row_ptr_b, const int32_t* col_idx_b, int64_t slabs_b,
+                          int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                          hipStream_t stream);
 
 /* Selection rule of vsa_mask_nabla. */
 typedef struct {

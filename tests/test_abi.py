@@ -145,3 +145,37 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 64, 2, 8)
     with pytest.raises(ValueError):
         vsa.vsa_tile_reorder(x, (4, 4, 4), (2, 2, 2))
+
+
+def sta_heads(L, grid=(8, 16, 16), tile=(4, 4, 4), windows=((1, 3, 3), (3, 3, 1)), batch=2,
+              rp=FAKE, ci=FAKE, cap=10 ** 6, null_windows=False):
+    flat = [x for w in windows for x in w]
+    arr = (ctypes.c_int32 * max(1, len(flat)))(*flat)
+    wptr = NULL if null_windows else ctypes.cast(arr, ctypes.c_void_p)
+    return L.vsa_mask_sta_heads(*grid, *tile, wptr, len(windows), batch, rp, ci, cap, NULL)
+
+
+def test_sta_heads_validation(L):
+    assert sta_heads(L, null_windows=True) == E_NULL
+    assert sta_heads(L, rp=NULL) == E_NULL
+    assert sta_heads(L, grid=(8, 16, 15)) == E_SHAPE
+    assert sta_heads(L, batch=0) == E_SHAPE
+    assert sta_heads(L, windows=((1, 3, 3), (2, 3, 3))) == E_PARAM
+    assert sta_heads(L, windows=((1, 3, 3), (1, -1, 3))) == E_PARAM
+    assert sta_heads(L, windows=((1, 1, 1),) * 257) == E_UNSUP
+    # bound = batch * (32 tiles * 1*3*3 + 32 tiles * 2*3*1): windows clipped to the 2x4x4 grid
+    assert sta_heads(L, cap=2 * (32 * 9 + 32 * 6) - 1) == E_CAP
+
+
+def union(L, nq=10, nk=7, rpa=FAKE, cia=FAKE, sa=1, rpb=FAKE, cib=FAKE, sb=4, rp=FAKE, ci=FAKE, cap=10 ** 6):
+    return L.vsa_mask_union(nq, nk, rpa, cia, sa, rpb, cib, sb, rp, ci, cap, NULL)
+
+
+def test_union_validation(L):
+    assert union(L, cia=NULL) == E_NULL
+    assert union(L, ci=NULL) == E_NULL
+    assert union(L, nq=0) == E_SHAPE
+    assert union(L, sa=0) == E_SHAPE
+    assert union(L, sa=2, sb=4) == E_PARAM
+    assert union(L, cap=4 * 10 * 7 - 1) == E_CAP
+    assert union(L, nq=2 ** 20, nk=2 ** 12, sb=1) == E_SHAPE

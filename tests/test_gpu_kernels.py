@@ -69,6 +69,35 @@ def test_mask_radial_bit_exact(T, S, block):
     assert np.array_equal(rp, orp) and np.array_equal(ci, oci)
 
 
+@pytest.mark.parametrize("grid,tile,windows,batch", [
+    ((8, 16, 16), (4, 4, 4), [(1, 3, 3), (3, 1, 1), (1, 1, 1), (3, 3, 3)], 2),
+    ((30, 48, 80), (6, 8, 8), [(3, 3, 5), (1, 3, 3), (5, 5, 9)], 1),
+    ((12, 12, 12), (2, 2, 2), [(13, 13, 13), (3, 5, 7)], 3),           # a window wider than the grid
+])
+def test_mask_sta_heads_bit_exact(grid, tile, windows, batch):
+    rp, ci = csr_np(*vsa.vsa_mask_sta_heads(grid, tile, windows, DEV, batch=batch))
+    orp, oci = oracle.mask_sta_heads(grid, tile, windows, batch)
+    assert np.array_equal(rp, orp) and np.array_equal(ci, oci)
+
+
+@pytest.mark.parametrize("nq,nk,slabs_a,slabs_b,da,db", [
+    (9, 13, 1, 1, 0.3, 0.4), (20, 300, 3, 3, 0.5, 0.2),      # rows longer than a wave
+    (16, 40, 1, 4, 0.1, 0.6), (16, 40, 4, 1, 0.6, 0.0),      # shared one-slab masks; an empty mask
+    (7, 2000, 2, 2, 0.9, 0.9),                                # long, mostly overlapping rows
+])
+def test_mask_union_bit_exact(nq, nk, slabs_a, slabs_b, da, db):
+    rng = np.random.default_rng(nq * 1000 + nk)
+    ka = rng.random((slabs_a * nq, nk)) < da
+    kb = rng.random((slabs_b * nq, nk)) < db
+    ka[0] = False                                             # an empty row in A
+    rpa, cia = oracle.csr_from_bool(ka)
+    rpb, cib = oracle.csr_from_bool(kb)
+    dev = lambda x: torch.from_numpy(np.concatenate([x, np.zeros(1, np.int32)]) if len(x) == 0 else x).to(DEV)
+    rp, ci = csr_np(*vsa.vsa_mask_union(dev(rpa), dev(cia), slabs_a, dev(rpb), dev(cib), slabs_b, nq, nk))
+    orp, oci = oracle.mask_union(rpa, cia, slabs_a, rpb, cib, slabs_b, nq)
+    assert np.array_equal(rp, orp) and np.array_equal(ci, oci)
+
+
 def _compare_selected(rp, ci, orp, oci, exempt):
     bad = []
     for r in range(len(orp) - 1):

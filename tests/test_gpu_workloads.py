@@ -205,3 +205,54 @@ def test_ar_chunk_workload():
     err = np.abs(o.cpu().double().numpy() - o_ref)
     log(f"ar: all rows max_abs={err.max():.2e} mean_abs={err.mean():.2e}")
     assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN
+
+
+# ------------------------------------------------------------- composition
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+def test_sta_heads_workload():
+    cfg = CONFIGS["sta_heads"]
+    grid, tile, H = cfg["grid"], cfg["tile"], cfg["heads"]
+    wins = [cfg["windows"][h % len(cfg["windows"])] for h in range(H)]
+    t0 = time.time()
+    x = gen.make_inputs("sta_heads")
+    o, rp_d, ci_d = _run_path(x, grid, tile, lambda q, k: vsa.vsa_mask_sta_heads(grid, tile, wins, DEV),
+                              384, H)
+    rp, ci = csr_np(rp_d, ci_d)
+    orp, oci = oracle.mask_sta_heads(grid, tile, wins, 1)
+    assert np.array_equal(rp, orp) and np.array_equal(ci, oci)
+    perm = oracle.tile_order_source(grid, tile)
+    mx, mn = _sampled_rows_check("sta_heads", x, o, rp, ci, 384, 384, H, perm=perm)
+    log(f"sta_heads: nnz={len(ci)} 4096 rows max_abs={mx:.2e} mean_abs={mn:.2e} ({time.time() - t0:.1f}s)")
+    assert mx <= BF16_MAX and mn <= BF16_MEAN
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_nabla_sta_workload():
+    cfg = CONFIGS["nabla_sta"]
+    grid, tile, thr, window = cfg["grid"], cfg["tile"], cfg["threshold"], cfg["window"]
+    H = cfg["heads"]
+    scale = 128 ** -0.5
+    t0 = time.time()
+    x = gen.make_inputs("nabla_sta")
+
+    def fn(q, k):
+        rpn, cin = vsa.vsa_mask_nabla(q, k, 64, 64, scale, threshold=thr)
+        rps, cis = vsa.vsa_mask_sta(grid, tile, window, DEV)
+        return vsa.vsa_mask_union(rpn, cin, H, rps, cis, 1, 960, 960)
+    o, rp_d, ci_d = _run_path(x, grid, tile, fn, 64, H)
+    rp, ci = csr_np(rp_d, ci_d)
+    perm = oracle.tile_order_source(grid, tile)
+    qt = x["q"][:, perm].double().numpy()
+    kt = x["k"][:, perm].double().numpy()
+    orp_n, oci_n, fl, nt = oracle.mask_nabla(qt, kt, 64, 64, scale, thr)
+    del qt, kt
+    orp_s, oci_s = oracle.mask_sta(grid, tile, window)
+    orp, oci = oracle.mask_union(orp_n, oci_n, H, orp_s, oci_s, 1, 960)
+    bad, n_ex = _compare_masks(rp, ci, orp, oci, fl | nt)
+    log(f"nabla_sta: nnz={len(ci)} (nabla alone {len(oci_n)}), flagged rows that differ {n_ex}")
+    assert not bad, f"unflagged mismatching rows: {bad[:10]}"
+    mx, mn = _sampled_rows_check("nabla_sta", x, o, rp, ci, 64, 64, H, perm=perm)
+    log(f"nabla_sta: 4096 rows max_abs={mx:.2e} mean_abs={mn:.2e} ({time.time() - t0:.1f}s)")
+    assert mx <= BF16_MAX and mn <= BF16_MEAN

@@ -1,4 +1,4 @@
-"""The five synthetic workloads, as plain data (shapes, dtypes, seeds, mask knobs).
+"""The synthetic workloads, as plain data (shapes, dtypes, seeds, mask knobs).
 
 Nothing here computes any part of the method; both the fp64 oracle and the GPU
 path read these numbers. Each workload is named by what it is:
@@ -21,6 +21,10 @@ path read these numbers. Each workload is named by what it is:
             tokens), 64-token raster blocks; anchors (frame 0) + the last 3 frames +
             the top-16 other blocks per query block (Sparse Forcing summary,
             gist.science/ja/paper/2604.21221, part 2).
+  nabla_sta -- the nabla workload with the NABLA mask united with a 3x3x5 STA
+            window on its 16x6x10 tile grid (NABLA explainer, sec. 2 and 4).
+  sta_heads -- the sta workload with a window per head, cycling 3x3x5, 1x3x3,
+            3x5x7 over the heads (STA explainer, sec. 1: heads specialise).
 
 Value model (synthetic stand-in for model activations; the pages give no
 statistics): Q = a*N(0,1) + P, K = a*N(0,1) + P, V = c*N(0,1) (+ P for `ar`), where
@@ -49,6 +53,17 @@ CONFIGS = {
     "radial": dict(
         seed=4, batch=1, heads=24, head_dim=128, dtype="bf16",
         grid=(125, 45, 80), block=128,
+        qk_noise=0.5, positional=True, v_positional=False,
+    ),
+    # Mask composition on the NABLA and STA inputs (same seeds, hence the same tensors).
+    "nabla_sta": dict(
+        seed=3, batch=1, heads=40, head_dim=128, dtype="bf16",
+        grid=(16, 48, 80), tile=(1, 8, 8), threshold=0.8, window=(3, 3, 5),
+        qk_noise=0.5, positional=True, v_positional=False,
+    ),
+    "sta_heads": dict(
+        seed=2, batch=1, heads=24, head_dim=128, dtype="bf16",
+        grid=(30, 48, 80), tile=(6, 8, 8), windows=((3, 3, 5), (1, 3, 3), (3, 5, 7)),
         qk_noise=0.5, positional=True, v_positional=False,
     ),
     "ar": dict(
