@@ -20,6 +20,8 @@ from the pages, step by step, in fp64 (numpy):
   masks.mask_sta_heads   -- STA with a window per head (STA explainer, sec. 1)
   masks.mask_union       -- union of two masks, e.g. NABLA with STA (NABLA
                             explainer, sec. 2 and 4)
+  sics.block_sics        -- SPADE's sum of intra-block cosine similarities
+                            (SPADE summary, gist.science/ja/paper/2608.03335)
   attention.attention    -- exact softmax(Q K^T * scale) V over the kept blocks
 
 Where the pages leave a step open, the reading taken is stated in the function.
@@ -31,3 +33,4 @@ from .masks import (  # noqa: F401
     mask_sta_heads, mask_union, csr_concat,
 )
 from .attention import attention, attention_rows, block_softmax  # noqa: F401
+from .sics import block_sics  # noqa: F401
