@@ -281,6 +281,28 @@ def main():
                  "speedup_vs_dense": float(np.mean(dms)) / attn_ms}
         print(f"[bench] dense run {dense['ms']:.2f} ms ({dense['tflops']:.1f} TFLOP/s)", file=sys.stderr, flush=True)
 
+    # SICS block scores (SPADE's scheme-step score) of the attention-order K, timed on their
+    # own, outside the step: HBM-bound, reported against the HBM peak and as a fraction of
+    # the attention time.
+    sics_out = torch.empty((path.B, path.H, path.nbk), dtype=torch.float64, device=dev)
+    path.vsa.vsa_block_sics(path.ka, path.bk, out=sics_out)
+    sms = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        path.vsa.vsa_block_sics(path.ka, path.bk, out=sics_out)
+        b.record(stream)
+        b.synchronize()
+        sms.append(a.elapsed_time(b))
+    sics_ms = float(np.mean(sms))
+    sics_bytes = path.ka.numel() * path.ka.element_size()
+    sics = {"ms": round(sics_ms, 4), "gbs": round(sics_bytes / (sics_ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(sics_bytes / (sics_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "ratio_to_attn": round(sics_ms / attn_ms, 5), "bytes": sics_bytes,
+            "kernel": "sics_kernel", "tensor": "K in attention order", "block": path.bk}
+    print(f"[bench] SICS of K: {sics_ms:.3f} ms, {sics['gbs']:.0f} GB/s ({100 * sics['frac_hbm']:.1f}% of HBM), "
+          f"{100 * sics['ratio_to_attn']:.2f}% of attention", file=sys.stderr, flush=True)
+
     traffic = None
     if name == "sta" and os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -324,6 +346,7 @@ def main():
         "dense_ms": None if dense is None else round(dense["ms"], 3),
         "dense_tflops": None if dense is None else round(dense["tflops"], 2),
         "stage_ms": {k_: round(float(np.mean(v_)), 4) for k_, v_ in ev.items()},
+        "sics": sics,
         "mask_over_attn": round(float(np.mean(ev["mask"])) / attn_ms, 5),
         "reorder_gbs": (round(4 * 2 * token_bytes / (reorder_ms * 1e-3) / 1e9, 1) if path.tiled else None),
     }

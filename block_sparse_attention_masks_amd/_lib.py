@@ -37,6 +37,7 @@ _SIGS = {
     "vsa_mask_radial": ([_I32, _I32, _I32, _P, _P, _I64, _P], _I32),
     "vsa_mask_sta_heads": ([_I32] * 6 + [_P, _I32, _I64, _P, _P, _I64, _P], _I32),
     "vsa_mask_union": ([_I64, _I32, _P, _P, _I64, _P, _P, _I64, _P, _P, _I64, _P], _I32),
+    "vsa_block_sics": ([_P, _I32, _I64, _I32, _I32, _I64, _I32, _P, _P], _I32),
     "vsa_mask_nabla": ([_P, _P, _I32, _I64, _I32, _I32, _I64, _I64, _I32, _I32, _F64,
                         ctypes.POINTER(Select), _P, _P, _I64, _P, ctypes.POINTER(ctypes.c_size_t), _P], _I32),
     "vsa_block_sparse_attn_fwd": ([_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I64, _I64, _I32, _I32,
@@ -193,6 +194,22 @@ def vsa_mask_union(rp_a, ci_a, slabs_a, rp_b, ci_b, slabs_b, n_qblocks, n_kblock
                                 slabs_b, _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), _stream(row_ptr)),
            "vsa_mask_union")
     return row_ptr, col_idx
+
+
+def vsa_block_sics(x, block, out=None):
+    """SICS block scores of x [B, N, heads, head_dim] (bf16 or fp32) -> fp64 [B, heads, ceil(N / block)]."""
+    _require(x, "x")
+    if x.dtype not in _DTYPE:
+        raise ValueError("x must be float32 or bfloat16")
+    B, N, H, D = x.shape
+    nb = -(-N // block)
+    out = torch.empty((B, H, nb), dtype=torch.float64, device=x.device) if out is None else out
+    _require(out, "out", x.device)
+    if out.dtype != torch.float64 or tuple(out.shape) != (B, H, nb):
+        raise ValueError("out must be float64 [B, heads, n_blocks]")
+    _check(lib().vsa_block_sics(_ptr(x), _DTYPE[x.dtype], B, H, D, N, block, _ptr(out), _stream(x)),
+           "vsa_block_sics")
+    return out
 
 
 def _select(threshold, topk, forced):

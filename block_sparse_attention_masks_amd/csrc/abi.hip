@@ -139,6 +139,17 @@ vsa_status vsa_mask_union(int64_t n_qblocks, int32_t n_kblocks, const int32_t* r
   return from_hip(vsa::launch_mask_union(u, rows, row_ptr, col_idx, stream));
 }
 
+vsa_status vsa_block_sics(const void* x, int32_t dtype, int64_t batch, int32_t heads, int32_t head_dim,
+                          int64_t n, int32_t block, double* scores, hipStream_t stream) {
+  if (!x || !scores) return VSA_ERR_NULL;
+  const vsa_status st = check_tokens(dtype, batch, heads, head_dim, n, n, block, block);
+  if (st != VSA_OK) return st;
+  if (!aligned16(x)) return VSA_ERR_UNSUPPORTED;
+  if (ceil_div(n, block) > 0x7fffffff / 2 || batch > 65535) return VSA_ERR_SHAPE;
+  return from_hip(vsa::launch_block_sics(x, dtype == VSA_BF16, batch, heads, head_dim, n, block, scores,
+                                         stream));
+}
+
 vsa_status vsa_mask_nabla(const void* q, const void* k, int32_t dtype, int64_t batch,
                           int32_t heads, int32_t head_dim, int64_t nq, int64_t nk,
                           int32_t block_q, int32_t block_k, double scale, const vsa_select* sel,

@@ -58,6 +58,10 @@ struct UnionArgs {
 hipError_t launch_mask_union(const UnionArgs& u, int64_t n_rows, int32_t* row_ptr, int32_t* col_idx,
                              hipStream_t stream);
 
+// SICS block scores of x [batch, n, heads, D] -> scores [batch, heads, ceil(n / block)] fp64.
+hipError_t launch_block_sics(const void* x, int bf16, int64_t batch, int heads, int D, int64_t n, int block,
+                             double* scores, hipStream_t stream);
+
 struct NablaArgs {
   const void* q;
   const void* k;

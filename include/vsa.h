@@ -165,6 +165,26 @@ vsa_status vsa_mask_union(int64_t n_qblocks, int32_t n_kblocks,
                           int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
                           hipStream_t stream);
 
+/*
+ * vsa_block_sics -- SICS block scores: sum of intra-block cosine similarities.
+ *
+ * SPADE summary (gist.science/ja/paper/2608.03335), "The solution" part 2: the
+ * scheme step groups tokens into blocks and scores how strongly each group's
+ * members agree.  Score of block i of head h = sum over all ordered token pairs
+ * (a, b) of the block, a = b included, of cos(x_a, x_b) = |sum_a x_a / |x_a||^2;
+ * a zero token row contributes nothing.  Computed in fp64.  Which tensor to score
+ * (Q or K) and how to select blocks from the scores are the caller's choice; the
+ * page states neither.
+ *
+ * x        device, [batch, n, heads, head_dim] (dtype VSA_F32 or VSA_BF16), 16-byte
+ *          aligned; head_dim 64 or 128.
+ * scores   device, [batch, heads, ceil(n / block)] doubles.
+ * Errors: VSA_ERR_NULL, VSA_ERR_DTYPE, VSA_ERR_SHAPE, VSA_ERR_UNSUPPORTED
+ * (head_dim, alignment), VSA_ERR_HIP.
+ */
+vsa_status vsa_block_sics(const void* x, int32_t dtype, int64_t batch, int32_t heads, int32_t head_dim,
+                          int64_t n, int32_t block, double* scores, hipStream_t stream);
+
 /* Selection rule of vsa_mask_nabla. */
 typedef struct {
   double cdf_threshold;   /* NABLA cut, in (0, 1]; used when topk == 0           */

@@ -179,3 +179,17 @@ def test_union_validation(L):
     assert union(L, sa=2, sb=4) == E_PARAM
     assert union(L, cap=4 * 10 * 7 - 1) == E_CAP
     assert union(L, nq=2 ** 20, nk=2 ** 12, sb=1) == E_SHAPE
+
+
+def sics(L, x=FAKE, dtype=1, B=1, H=2, D=128, n=1000, block=64, out=FAKE):
+    return L.vsa_block_sics(x, dtype, B, H, D, n, block, out, NULL)
+
+
+def test_sics_validation(L):
+    assert sics(L, x=NULL) == E_NULL
+    assert sics(L, out=NULL) == E_NULL
+    assert sics(L, dtype=5) == E_DTYPE
+    assert sics(L, D=96) == E_UNSUP
+    assert sics(L, n=0) == E_SHAPE
+    assert sics(L, block=0) == E_SHAPE
+    assert sics(L, x=ODD) == E_UNSUP

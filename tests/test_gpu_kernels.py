@@ -193,3 +193,20 @@ def test_attention_deterministic_and_dense_mask():
         *(t.double().cpu().permute(0, 2, 1, 3) for t in (q, k, v))).permute(0, 2, 1, 3)
     err = (o1.double().cpu() - ref).abs()
     assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN
+
+
+# ------------------------------------------------------------------------ SICS
+@pytest.mark.parametrize("B,N,H,D,block,dtype", [
+    (1, 1000, 2, 128, 64, torch.bfloat16),      # ragged tail block
+    (2, 300, 3, 64, 7, torch.float32),
+    (1, 130, 40, 128, 384, torch.bfloat16),     # one short block; 640 vectors per row -> two slices
+    (1, 65, 1, 64, 1, torch.bfloat16),          # one-row blocks score 1
+])
+def test_block_sics_matches_oracle(B, N, H, D, block, dtype):
+    x = rand((B, N, H, D), dtype, 31)
+    x[:, 3] = 0                                  # zero rows add nothing
+    got = vsa.vsa_block_sics(x.to(DEV), block).cpu().numpy()
+    want = oracle.block_sics(x.double().numpy(), block)
+    assert np.allclose(got, want, rtol=1e-10, atol=1e-10)
+    if block == 1:
+        assert np.all(np.isclose(got, 1.0, rtol=0, atol=1e-14) | (got == 0.0))

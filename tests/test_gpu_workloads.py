@@ -256,3 +256,26 @@ def test_nabla_sta_workload():
     mx, mn = _sampled_rows_check("nabla_sta", x, o, rp, ci, 64, 64, H, perm=perm)
     log(f"nabla_sta: 4096 rows max_abs={mx:.2e} mean_abs={mn:.2e} ({time.time() - t0:.1f}s)")
     assert mx <= BF16_MAX and mn <= BF16_MEAN
+
+
+# ------------------------------------------------------------------------ SICS
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+def test_sics_sta_workload():
+    """SICS scores of the tile-reordered K of the sta workload (24 heads x 300 blocks of
+    384 tokens); the oracle's pairwise definition on 240 sampled (head, block) pairs."""
+    cfg = CONFIGS["sta"]
+    grid, tile = cfg["grid"], cfg["tile"]
+    x = gen.make_inputs("sta")
+    kd = vsa.vsa_tile_reorder(x["k"].to(DEV), grid, tile)
+    got = vsa.vsa_block_sics(kd, 384).cpu().numpy()
+    perm = oracle.tile_order_source(grid, tile)
+    kt = x["k"][:, perm]
+    rng = np.random.default_rng(41)
+    worst = 0.0
+    for h, i in zip(rng.integers(0, 24, 240), rng.integers(0, 300, 240)):
+        rows = kt[:, i * 384:(i + 1) * 384, h:h + 1].double().numpy()
+        want = oracle.block_sics(rows, 384)[0, 0, 0]
+        worst = max(worst, abs(got[0, h, i] - want) / want)
+    log(f"sics/sta: score range {got.min():.1f}..{got.max():.1f}, worst relative error {worst:.2e}")
+    assert worst < 1e-10
