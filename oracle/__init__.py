@@ -22,6 +22,9 @@ from the pages, step by step, in fp64 (numpy):
                             explainer, sec. 2 and 4)
   sics.block_sics        -- SPADE's sum of intra-block cosine similarities
                             (SPADE summary, gist.science/ja/paper/2608.03335)
+  kvcache.kv_keep / kv_compact / mask_remap
+                         -- KV-cache compaction to the kept blocks (Sparse
+                            Forcing summary, parts 2-3)
   attention.attention    -- exact softmax(Q K^T * scale) V over the kept blocks
 
 Where the pages leave a step open, the reading taken is stated in the function.
@@ -34,3 +37,4 @@ from .masks import (  # noqa: F401
 )
 from .attention import attention, attention_rows, block_softmax  # noqa: F401
 from .sics import block_sics  # noqa: F401
+from . import kvcache  # noqa: F401
