@@ -6,8 +6,9 @@ the GPU with the inputs resident in HBM:
     [inverse reorder of O]
 The default workload is the STA one (24 heads, head_dim 128, bf16, 30x48x80 =
 115,200 tokens, 6x8x8 tiles = 384-token blocks on a 5x6x10 tile grid, 3x3x5 tile
-window clipped at the border); --workload nabla | radial | ar measures the
-others (their lines are reports, not the headline).
+window clipped at the border); --workload nabla | radial | ar | nabla_sta |
+sta_heads | ar_compact measures the others (their lines are reports, not the
+headline).
 
 value       = kept-block attention FLOPs (4 * D * sum of nq*nk over kept block
               pairs, true token counts) / wall time of a step, TFLOP/s.
@@ -51,6 +52,8 @@ DESCRIPTION = {
                  "window on the 16x6x10 tile grid",
     "sta_heads": "sta_heads: the sta workload with one tile window per head (3x3x5, 1x3x3, 3x5x7 cycling "
                  "over the 24 heads)",
+    "ar_compact": "ar_compact: the ar workload with its KV cache compacted to the blocks each head keeps "
+                  "(plan, gather K and V, mask remap) before attention",
     "ar": "ar: 1 x 12 heads, 4,680 query tokens (3x30x52 chunk) over a 32,760-token KV cache "
           "(21x30x52), head_dim 128, bf16, 64-token blocks, anchors + last 3 frames + top-16",
 }
@@ -185,6 +188,29 @@ class Path:
                                                        workspace=ws, row_ptr=self.rp, col_idx=self.ci,
                                                        **sel)
         self.ci = torch.empty(cap, dtype=torch.int32, device=dev)
+        self.compact = None
+        if name == "ar_compact":
+            # size the compact cache once (the inputs are fixed); the step itself allocates nothing
+            self.mask()
+            slot, info = vsa.vsa_kv_plan(self.rp, self.ci, self.n_slabs, nbq, self.nk, self.bk)
+            self.n_out = vsa.compact_tokens(info[:2].cpu().tolist(), self.nk, self.bk)
+            self.slot, self.info = slot, info
+            self.kc = torch.empty((B, self.n_out, H, D), dtype=self.k.dtype, device=dev)
+            self.vc = torch.empty_like(self.kc)
+            self.cc = torch.empty_like(self.ci)
+
+            def compact():
+                vsa.vsa_kv_plan(self.rp, self.ci, self.n_slabs, nbq, self.nk, self.bk, slot=self.slot, info=self.info)
+                vsa.vsa_kv_gather(self.k, self.slot, self.n_slabs, self.bk, self.n_out, out=self.kc)
+                vsa.vsa_kv_gather(self.v, self.slot, self.n_slabs, self.bk, self.n_out, out=self.vc)
+                vsa.vsa_mask_remap(self.rp, self.ci, self.n_slabs, nbq, self.slot, nbk, out=self.cc)
+            self.compact = compact
+
+    def stages(self):
+        out = [("reorder_in", self.reorder_in), ("mask", self.mask)]
+        if self.compact is not None:
+            out.append(("compact", self.compact))
+        return out + [("attn", self.attn), ("reorder_out", self.reorder_out)]
 
     def reorder_in(self):
         if self.tiled:
@@ -192,6 +218,10 @@ class Path:
                 self.vsa.vsa_tile_reorder(src, *self.tiled, out=dst)
 
     def attn(self, rp=None, ci=None):
+        if rp is None and self.compact is not None:   # over the compact cache
+            self.vsa.vsa_block_sparse_attn_fwd(self.qa, self.kc, self.vc, self.rp, self.cc, self.bq, self.bk,
+                                               self.n_slabs, self.scale, out=self.oa, lse=self.lse)
+            return
         self.vsa.vsa_block_sparse_attn_fwd(self.qa, self.ka, self.va, self.rp if rp is None else rp,
                                            self.ci if ci is None else ci, self.bq, self.bk,
                                            self.n_slabs if rp is None else 1, self.scale,
@@ -229,17 +259,18 @@ def main():
     print(f"[bench] {name}: inputs generated in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
     path = Path(name, cfg, x, dev)
     stream = torch.cuda.current_stream(dev)
-    stages = ("reorder_in", "mask", "attn", "reorder_out")
+    stage_fns = path.stages()
+    stages = tuple(n_ for n_, _ in stage_fns)
     ev = {s: [] for s in stages}
 
     def step(record):
-        marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
-        for i, fn in enumerate((path.reorder_in, path.mask, path.attn, path.reorder_out)):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(stage_fns) + 1)] if record else None
+        for i, (_, fn) in enumerate(stage_fns):
             if record:
                 marks[i].record(stream)
             fn()
         if record:
-            marks[4].record(stream)
+            marks[-1].record(stream)
         return marks
 
     for _ in range(args.warmup):
@@ -347,6 +378,11 @@ def main():
         "dense_tflops": None if dense is None else round(dense["tflops"], 2),
         "stage_ms": {k_: round(float(np.mean(v_)), 4) for k_, v_ in ev.items()},
         "sics": sics,
+        "kv_compaction": (None if path.compact is None else
+                          {"tokens_before": path.nk, "tokens_after": path.n_out,
+                           "reduction": round(1 - path.n_out / path.nk, 4),
+                           "ms": round(float(np.mean(ev["compact"])), 4),
+                           "bytes_moved": 2 * 2 * path.B * path.n_out * path.H * path.D * path.k.element_size()}),
         "mask_over_attn": round(float(np.mean(ev["mask"])) / attn_ms, 5),
         "reorder_gbs": (round(4 * 2 * token_bytes / (reorder_ms * 1e-3) / 1e9, 1) if path.tiled else None),
     }

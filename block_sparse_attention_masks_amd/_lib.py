@@ -38,6 +38,9 @@ _SIGS = {
     "vsa_mask_sta_heads": ([_I32] * 6 + [_P, _I32, _I64, _P, _P, _I64, _P], _I32),
     "vsa_mask_union": ([_I64, _I32, _P, _P, _I64, _P, _P, _I64, _P, _P, _I64, _P], _I32),
     "vsa_block_sics": ([_P, _I32, _I64, _I32, _I32, _I64, _I32, _P, _P], _I32),
+    "vsa_kv_plan": ([_P, _P, _I64, _I64, _I64, _I32, _P, _P, _P], _I32),
+    "vsa_kv_gather": ([_P, _I32, _I64, _I32, _I32, _I64, _I32, _P, _I64, _P, _I64, _P], _I32),
+    "vsa_mask_remap": ([_P, _P, _I64, _I64, _P, _I32, _P, _P], _I32),
     "vsa_mask_nabla": ([_P, _P, _I32, _I64, _I32, _I32, _I64, _I64, _I32, _I32, _F64,
                         ctypes.POINTER(Select), _P, _P, _I64, _P, ctypes.POINTER(ctypes.c_size_t), _P], _I32),
     "vsa_block_sparse_attn_fwd": ([_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I64, _I64, _I32, _I32,
@@ -210,6 +213,75 @@ def vsa_block_sics(x, block, out=None):
     _check(lib().vsa_block_sics(_ptr(x), _DTYPE[x.dtype], B, H, D, N, block, _ptr(out), _stream(x)),
            "vsa_block_sics")
     return out
+
+
+def vsa_kv_plan(row_ptr, col_idx, n_slabs, n_qblocks, nk, block_k, slot=None, info=None):
+    """Slot map of each mask slab -> (slot int32 [n_slabs, n_kblocks], info int32 [2 + 2 n_slabs])."""
+    _require(row_ptr, "row_ptr")
+    _require(col_idx, "col_idx", row_ptr.device)
+    nbk = -(-nk // block_k)
+    if slot is None:
+        slot = torch.empty((n_slabs, nbk), dtype=torch.int32, device=row_ptr.device)
+    if info is None:
+        info = torch.empty(2 + 2 * n_slabs, dtype=torch.int32, device=row_ptr.device)
+    _require(slot, "slot", row_ptr.device)
+    _require(info, "info", row_ptr.device)
+    if slot.numel() != n_slabs * nbk or info.numel() != 2 + 2 * n_slabs:
+        raise ValueError("slot must hold n_slabs * n_kblocks ints and info 2 + 2 * n_slabs")
+    if row_ptr.numel() != n_slabs * n_qblocks + 1:
+        raise ValueError("row_ptr must hold n_slabs * n_qblocks + 1 entries")
+    _check(lib().vsa_kv_plan(_ptr(row_ptr), _ptr(col_idx), n_slabs, n_qblocks, nk, block_k, _ptr(slot), _ptr(info),
+                             _stream(row_ptr)), "vsa_kv_plan")
+    return slot, info
+
+
+def compact_tokens(info, nk, block_k):
+    """Token count of the compact cache from the plan's info (host ints or tensor)."""
+    n_full, has_tail = int(info[0]), int(info[1])
+    return n_full * block_k + ((nk % block_k) if has_tail else 0)
+
+
+def vsa_kv_gather(x, slot, n_slabs, block_k, n_out, out=None):
+    """Kept blocks of x [B, nk, heads, head_dim] -> compact cache [B, n_out, heads, head_dim]."""
+    _require(x, "x")
+    if x.dtype not in _DTYPE:
+        raise ValueError("x must be float32 or bfloat16")
+    B, nk, H, D = x.shape
+    if out is None:
+        out = torch.empty((B, n_out, H, D), dtype=x.dtype, device=x.device)
+    _require(out, "out", x.device)
+    _require(slot, "slot", x.device)
+    if out.dtype != x.dtype or tuple(out.shape) != (B, n_out, H, D):
+        raise ValueError("out must match x's dtype and be [B, n_out, heads, head_dim]")
+    _check(lib().vsa_kv_gather(_ptr(x), _DTYPE[x.dtype], B, H, D, nk, block_k, _ptr(slot), n_slabs, _ptr(out),
+                               n_out, _stream(x)), "vsa_kv_gather")
+    return out
+
+
+def vsa_mask_remap(row_ptr, col_idx, n_slabs, n_qblocks, slot, n_kblocks, out=None):
+    """Mask columns rewritten to compact slots (row_ptr unchanged) -> col_idx tensor."""
+    _require(row_ptr, "row_ptr")
+    _require(col_idx, "col_idx", row_ptr.device)
+    _require(slot, "slot", row_ptr.device)
+    if out is None:
+        out = torch.empty_like(col_idx)
+    _require(out, "out", row_ptr.device)
+    _check(lib().vsa_mask_remap(_ptr(row_ptr), _ptr(col_idx), n_slabs, n_qblocks, _ptr(slot), n_kblocks, _ptr(out),
+                                _stream(row_ptr)), "vsa_mask_remap")
+    return out
+
+
+def vsa_kv_compact(k, v, row_ptr, col_idx, n_slabs, block_q, block_k):
+    """Plan, gather K and V, and rewrite the mask (one host sync to size the cache).
+    Returns (k_compact, v_compact, col_idx_compact, n_out, slot, info)."""
+    nq_blocks = (row_ptr.numel() - 1) // n_slabs
+    nk = k.shape[1]
+    slot, info = vsa_kv_plan(row_ptr, col_idx, n_slabs, nq_blocks, nk, block_k)
+    n_out = compact_tokens(info[:2].cpu().tolist(), nk, block_k)
+    kc = vsa_kv_gather(k, slot, n_slabs, block_k, n_out)
+    vc = vsa_kv_gather(v, slot, n_slabs, block_k, n_out)
+    cc = vsa_mask_remap(row_ptr, col_idx, n_slabs, nq_blocks, slot, -(-nk // block_k))
+    return kc, vc, cc, n_out, slot, info
 
 
 def _select(threshold, topk, forced):

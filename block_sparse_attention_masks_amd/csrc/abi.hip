@@ -150,6 +150,42 @@ vsa_status vsa_block_sics(const void* x, int32_t dtype, int64_t batch, int32_t h
                                          stream));
 }
 
+vsa_status vsa_kv_plan(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_slabs, int64_t n_qblocks,
+                       int64_t nk, int32_t block_k, int32_t* slot, int32_t* info, hipStream_t stream) {
+  if (!row_ptr || !col_idx || !slot || !info) return VSA_ERR_NULL;
+  if (n_slabs <= 0 || n_qblocks <= 0 || nk <= 0 || block_k <= 0) return VSA_ERR_SHAPE;
+  const int64_t nbk = ceil_div(nk, block_k);
+  if (nbk > kI32Max || n_slabs > kI32Max || n_slabs * n_qblocks > kI32Max) return VSA_ERR_SHAPE;
+  const int tail = nk % block_k ? (int)nbk - 1 : -1;
+  return from_hip(vsa::launch_kv_plan(row_ptr, col_idx, n_slabs, n_qblocks, (int)nbk, tail, slot, info, stream));
+}
+
+vsa_status vsa_kv_gather(const void* x, int32_t dtype, int64_t batch, int32_t heads, int32_t head_dim,
+                         int64_t nk, int32_t block_k, const int32_t* slot, int64_t n_slabs, void* out,
+                         int64_t n_out, hipStream_t stream) {
+  if (!x || !slot || !out) return VSA_ERR_NULL;
+  const vsa_status st = check_tokens(dtype, batch, heads, head_dim, nk, nk, block_k, block_k);
+  if (st != VSA_OK) return st;
+  if (n_out <= 0 || n_out > kI32Max || batch > 65535) return VSA_ERR_SHAPE;
+  if (n_slabs != 1 && n_slabs != batch * heads) return VSA_ERR_PARAM;
+  if (!aligned16(x) || !aligned16(out)) return VSA_ERR_UNSUPPORTED;
+  const int64_t nbk = ceil_div(nk, block_k);
+  if (nbk * ((block_k + 7) / 8) > kI32Max) return VSA_ERR_SHAPE;
+  const int esz = dtype == VSA_BF16 ? 2 : 4;
+  const int row_vec = heads * head_dim * esz / 16;
+  return from_hip(vsa::launch_kv_gather(x, batch, nk, block_k, heads, row_vec, (int)nbk, slot, n_slabs, out,
+                                        n_out, stream));
+}
+
+vsa_status vsa_mask_remap(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_slabs, int64_t n_qblocks,
+                          const int32_t* slot, int32_t n_kblocks, int32_t* col_out, hipStream_t stream) {
+  if (!row_ptr || !col_idx || !slot || !col_out) return VSA_ERR_NULL;
+  if (n_slabs <= 0 || n_qblocks <= 0 || n_kblocks <= 0) return VSA_ERR_SHAPE;
+  if (n_slabs * n_qblocks > kI32Max) return VSA_ERR_SHAPE;
+  return from_hip(vsa::launch_mask_remap(row_ptr, col_idx, n_slabs * n_qblocks, n_qblocks, slot, n_kblocks,
+                                         n_slabs, col_out, stream));
+}
+
 vsa_status vsa_mask_nabla(const void* q, const void* k, int32_t dtype, int64_t batch,
                           int32_t heads, int32_t head_dim, int64_t nq, int64_t nk,
                           int32_t block_q, int32_t block_k, double scale, const vsa_select* sel,

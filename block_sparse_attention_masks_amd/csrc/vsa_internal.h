@@ -62,6 +62,16 @@ hipError_t launch_mask_union(const UnionArgs& u, int64_t n_rows, int32_t* row_pt
 hipError_t launch_block_sics(const void* x, int bf16, int64_t batch, int heads, int D, int64_t n, int block,
                              double* scores, hipStream_t stream);
 
+// KV-cache compaction: slot map per slab, gather into the compact cache, mask remap.
+hipError_t launch_kv_plan(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_slabs, int64_t n_qblocks,
+                          int n_kblocks, int tail, int32_t* slot, int32_t* info, hipStream_t stream);
+hipError_t launch_kv_gather(const void* x, int64_t batch, int64_t nk, int block_k, int heads, int row_vec,
+                            int n_kblocks, const int32_t* slot, int64_t n_slabs, void* out, int64_t n_out,
+                            hipStream_t stream);
+hipError_t launch_mask_remap(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_rows, int64_t n_qblocks,
+                             const int32_t* slot, int n_kblocks, int64_t n_slabs, int32_t* col_out,
+                             hipStream_t stream);
+
 struct NablaArgs {
   const void* q;
   const void* k;

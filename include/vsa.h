@@ -185,6 +185,47 @@ vsa_status vsa_mask_union(int64_t n_qblocks, int32_t n_kblocks,
 vsa_status vsa_block_sics(const void* x, int32_t dtype, int64_t batch, int32_t heads, int32_t head_dim,
                           int64_t n, int32_t block, double* scores, hipStream_t stream);
 
+/*
+ * KV-cache compaction for chunked autoregressive generation.
+ *
+ * Sparse Forcing summary (gist.science/ja/paper/2604.21221), parts 2-3: anchor
+ * blocks are kept as persistent memory and recent blocks only where needed; the
+ * rest of the past is not stored (42% less memory on the page).  A (batch, head)
+ * keeps the union of the key blocks its mask rows keep; the compact cache keeps
+ * the [batch, tokens, heads, head_dim] layout, each head's kept full blocks packed
+ * from slot 0 in ascending order and a kept ragged last block in one shared tail
+ * slot after the largest head's full blocks.  With the mask rewritten onto the
+ * slots, attention over the compact cache equals attention over the full cache.
+ *
+ * vsa_kv_plan -- slot map of each mask slab.
+ *   row_ptr/col_idx  device CSR mask, n_slabs * n_qblocks rows (1 slab = shared).
+ *   slot   device, n_slabs * ceil(nk / block_k) ints out: slot of each key block,
+ *          -1 if no row of the slab keeps it.
+ *   info   device, 2 + 2 * n_slabs ints out: info[0] = full blocks of the largest
+ *          slab (= the tail slot), info[1] = 1 if a slab keeps a ragged last block;
+ *          the rest is per-slab scratch.  The compact cache holds
+ *          info[0] * block_k + (info[1] ? nk % block_k : 0) tokens.
+ *   Errors: VSA_ERR_NULL, VSA_ERR_SHAPE, VSA_ERR_HIP.
+ *
+ * vsa_kv_gather -- copy the kept blocks of x [batch, nk, heads, head_dim] into out
+ *   [batch, n_out, heads, head_dim] (same dtype, 16-byte aligned); slot/n_slabs as
+ *   planned (n_slabs 1 or batch * heads).  Slots no kept block maps to are not
+ *   written; writes past n_out are dropped, so pass n_out from info.
+ *   Errors: VSA_ERR_NULL, VSA_ERR_DTYPE, VSA_ERR_SHAPE, VSA_ERR_PARAM (n_slabs),
+ *   VSA_ERR_UNSUPPORTED (head_dim, alignment), VSA_ERR_HIP.
+ *
+ * vsa_mask_remap -- col_out[e] = slot of col_idx[e] in its row's slab; row_ptr is
+ *   unchanged and rows stay ascending.  col_out device, row_ptr[n_rows] ints.
+ *   Errors: VSA_ERR_NULL, VSA_ERR_SHAPE, VSA_ERR_HIP.
+ */
+vsa_status vsa_kv_plan(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_slabs, int64_t n_qblocks,
+                       int64_t nk, int32_t block_k, int32_t* slot, int32_t* info, hipStream_t stream);
+vsa_status vsa_kv_gather(const void* x, int32_t dtype, int64_t batch, int32_t heads, int32_t head_dim,
+                         int64_t nk, int32_t block_k, const int32_t* slot, int64_t n_slabs, void* out,
+                         int64_t n_out, hipStream_t stream);
+vsa_status vsa_mask_remap(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_slabs, int64_t n_qblocks,
+                          const int32_t* slot, int32_t n_kblocks, int32_t* col_out, hipStream_t stream);
+
 /* Selection rule of vsa_mask_nabla. */
 typedef struct {
   double cdf_threshold;   /* NABLA cut, in (0, 1]; used when topk == 0           */

@@ -193,3 +193,19 @@ def test_sics_validation(L):
     assert sics(L, n=0) == E_SHAPE
     assert sics(L, block=0) == E_SHAPE
     assert sics(L, x=ODD) == E_UNSUP
+
+
+def test_kv_validation(L):
+    assert L.vsa_kv_plan(NULL, FAKE, 1, 4, 1000, 64, FAKE, FAKE, NULL) == E_NULL
+    assert L.vsa_kv_plan(FAKE, FAKE, 0, 4, 1000, 64, FAKE, FAKE, NULL) == E_SHAPE
+    assert L.vsa_kv_plan(FAKE, FAKE, 1, 4, 1000, 0, FAKE, FAKE, NULL) == E_SHAPE
+    g = lambda **kw: L.vsa_kv_gather(kw.get("x", FAKE), kw.get("dtype", 1), 1, 2, kw.get("D", 128), 1000, 64,
+                                     FAKE, kw.get("slabs", 2), kw.get("out", FAKE), kw.get("n_out", 500), NULL)
+    assert g(x=NULL) == E_NULL
+    assert g(dtype=3) == E_DTYPE
+    assert g(D=80) == E_UNSUP
+    assert g(slabs=3) == E_PARAM
+    assert g(n_out=0) == E_SHAPE
+    assert g(out=ODD) == E_UNSUP
+    assert L.vsa_mask_remap(FAKE, FAKE, 1, 4, NULL, 16, FAKE, NULL) == E_NULL
+    assert L.vsa_mask_remap(FAKE, FAKE, 1, 0, FAKE, 16, FAKE, NULL) == E_SHAPE

@@ -210,3 +210,42 @@ def test_block_sics_matches_oracle(B, N, H, D, block, dtype):
     assert np.allclose(got, want, rtol=1e-10, atol=1e-10)
     if block == 1:
         assert np.all(np.isclose(got, 1.0, rtol=0, atol=1e-14) | (got == 0.0))
+
+
+# ------------------------------------------------------------ KV compaction
+@pytest.mark.parametrize("B,H,D,nq,nk,bq,bk,slabs,dtype,tail_slabs", [
+    (1, 3, 128, 300, 1000, 64, 64, 3, torch.bfloat16, (0, 2)),   # ragged tail kept by two heads
+    (2, 2, 64, 200, 1024, 50, 64, 4, torch.bfloat16, None),      # no ragged tail
+    (1, 2, 128, 130, 777, 64, 96, 1, torch.float32, (0,)),        # one shared mask
+])
+def test_kv_compaction_matches_oracle(B, H, D, nq, nk, bq, bk, slabs, dtype, tail_slabs):
+    from oracle import kvcache
+    rng = np.random.default_rng(nk + bk)
+    nbq, nbk = -(-nq // bq), -(-nk // bk)
+    keep = rng.random((slabs * nbq, nbk)) < 0.2
+    keep[:, 0] = True
+    if nk % bk:
+        keep[:, -1] = False
+        for s in tail_slabs:
+            keep[s * nbq, -1] = True
+    rp, ci = oracle.csr_from_bool(keep)
+    k, v = rand((B, nk, H, D), dtype, 51), rand((B, nk, H, D), dtype, 52)
+    q = rand((B, nq, H, D), dtype, 53)
+    rpd, cid = torch.from_numpy(rp).to(DEV), torch.from_numpy(ci).to(DEV)
+    slot, info = vsa.vsa_kv_plan(rpd, cid, slabs, nbq, nk, bk)
+    _, remap, n_full_max, has_tail = kvcache.kv_keep(rp, ci, slabs, nbq, nbk, nk, bk)
+    assert np.array_equal(slot.cpu().numpy(), remap)
+    assert info[:2].cpu().tolist() == [n_full_max, int(has_tail)]
+    n_out = vsa.compact_tokens(info[:2].cpu().tolist(), nk, bk)
+    assert n_out == kvcache.compact_tokens(n_full_max, has_tail, nk, bk) and n_out < nk
+    kc = vsa.vsa_kv_gather(k.to(DEV), slot, slabs, bk, n_out, out=torch.zeros((B, n_out, H, D), dtype=dtype, device=DEV))
+    want = kvcache.kv_compact(k.numpy() if dtype == torch.float32 else k.view(torch.int16).numpy(), remap, H, bk, n_out)
+    got = kc.cpu()
+    assert np.array_equal(got.numpy() if dtype == torch.float32 else got.view(torch.int16).numpy(), want)
+    cc = vsa.vsa_mask_remap(rpd, cid, slabs, nbq, slot, nbk)
+    assert np.array_equal(cc.cpu().numpy(), kvcache.mask_remap(rp, ci, remap, nbq)[1])
+    # attention over the compact cache is the same computation, tile for tile
+    vc = vsa.vsa_kv_gather(v.to(DEV), slot, slabs, bk, n_out)
+    o_full, l_full = vsa.vsa_block_sparse_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), rpd, cid, bq, bk, slabs)
+    o_comp, l_comp = vsa.vsa_block_sparse_attn_fwd(q.to(DEV), kc, vc, rpd, cc, bq, bk, slabs)
+    assert torch.equal(o_full, o_comp) and torch.equal(l_full, l_comp)

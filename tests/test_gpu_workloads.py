@@ -279,3 +279,33 @@ def test_sics_sta_workload():
         worst = max(worst, abs(got[0, h, i] - want) / want)
     log(f"sics/sta: score range {got.min():.1f}..{got.max():.1f}, worst relative error {worst:.2e}")
     assert worst < 1e-10
+
+
+# ------------------------------------------------------------- KV compaction
+@pytest.mark.timeout(600)
+def test_ar_kv_compaction_workload():
+    """The ar chunk's KV cache compacted to the blocks its heads keep: the slot map equals
+    the oracle's on the GPU's mask, and attention over the compact cache equals
+    attention over the full cache bit for bit."""
+    from oracle import kvcache
+    cfg = CONFIGS["ar"]
+    T, Hg, Wg = cfg["grid"]
+    block, topk, H = cfg["block"], cfg["topk"], cfg["heads"]
+    scale = 128 ** -0.5
+    forced = vsa.ar_forced_ranges(Hg * Wg, T, cfg["anchor_frames"], cfg["recent_frames"], block)
+    x = gen.make_inputs("ar")
+    q, k, v = (x[w].to(DEV) for w in ("q", "k", "v"))
+    rp, ci = vsa.vsa_mask_nabla(q, k, block, block, scale, topk=topk, forced=forced)
+    nq, nk = q.shape[1], k.shape[1]
+    nbq, nbk = -(-nq // block), -(-nk // block)
+    kc, vc, cc, n_out, slot, info = vsa.vsa_kv_compact(k, v, rp, ci, H, block, block)
+    rph, cih = csr_np(rp, ci)
+    _, remap, n_full_max, has_tail = kvcache.kv_keep(rph, cih, H, nbq, nbk, nk, block)
+    assert np.array_equal(slot.cpu().numpy(), remap)
+    assert n_out == kvcache.compact_tokens(n_full_max, has_tail, nk, block)
+    kept = (remap >= 0).sum(axis=1)
+    log(f"ar kv: cache {nk} -> {n_out} tokens ({100 * (1 - n_out / nk):.1f}% smaller), kept blocks per head "
+        f"{kept.min()}..{kept.max()} of {nbk}")
+    o_full, l_full = vsa.vsa_block_sparse_attn_fwd(q, k, v, rp, ci, block, block, H, scale)
+    o_comp, l_comp = vsa.vsa_block_sparse_attn_fwd(q, kc, vc, rp, cc, block, block, H, scale)
+    assert torch.equal(o_full, o_comp) and torch.equal(l_full, l_comp)

@@ -25,6 +25,8 @@ path read these numbers. Each workload is named by what it is:
             window on its 16x6x10 tile grid (NABLA explainer, sec. 2 and 4).
   sta_heads -- the sta workload with a window per head, cycling 3x3x5, 1x3x3,
             3x5x7 over the heads (STA explainer, sec. 1: heads specialise).
+  ar_compact -- the ar workload with its KV cache compacted to the blocks each
+            head keeps before attention (Sparse Forcing summary, parts 2-3).
 
 Value model (synthetic stand-in for model activations; the pages give no
 statistics): Q = a*N(0,1) + P, K = a*N(0,1) + P, V = c*N(0,1) (+ P for `ar`), where
@@ -74,6 +76,9 @@ CONFIGS = {
         qk_noise=1.0, positional=True, v_positional=True,
     ),
 }
+
+# The ar chunk with its KV cache compacted to the blocks each head keeps (same inputs).
+CONFIGS["ar_compact"] = dict(CONFIGS["ar"])
 
 
 def n_tokens(grid):
