@@ -26,6 +26,7 @@ from the pages, step by step, in fp64 (numpy):
                          -- KV-cache compaction to the kept blocks (Sparse
                             Forcing summary, parts 2-3)
   attention.attention    -- exact softmax(Q K^T * scale) V over the kept blocks
+  attention.attention_bwd-- its gradients dQ, dK, dV (chain rule, step by step)
 
 Where the pages leave a step open, the reading taken is stated in the function.
 """
@@ -35,6 +36,6 @@ from .masks import (  # noqa: F401
     pool_blocks, nabla_select_row, mask_nabla, ar_forced_ranges, ar_select_row, mask_ar,
     mask_sta_heads, mask_union, csr_concat,
 )
-from .attention import attention, attention_rows, block_softmax  # noqa: F401
+from .attention import attention, attention_bwd, attention_rows, block_softmax  # noqa: F401
 from .sics import block_sics  # noqa: F401
 from . import kvcache  # noqa: F401

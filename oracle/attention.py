@@ -96,3 +96,47 @@ def attention_rows(q_rows, row_tokens, kh, vh, row_ptr, col_idx, row_base,
             out[c0:c1] = np.where(ok[:, None], (p @ vh) / l, 0.0)
             lse[c0:c1] = np.where(ok, (m + np.log(l))[:, 0], -np.inf)
     return out, lse
+
+
+def attention_bwd(q, k, v, dout, row_ptr, col_idx, block_q, block_k, scale, n_slabs=1):
+    """Gradients of L = sum(dout * o) for o = attention(q, k, v) over the kept blocks:
+    returns (dq, dk, dv) fp64 with the shapes of q, k, v.
+
+    The pages report that the sparse patterns also train (Radial Attention explainer,
+    sec. 4: faster training as well as inference; Sparse Forcing summary, part 2: the
+    model learns the sparse memory), so the path has a backward pass.  Reading taken:
+    the gradient of the same exact attention, evaluated by the chain rule step by
+    step for each query block i with key set J_i (no saved state):
+
+        s = q K^T * scale, p = softmax(s)          (rows of the block)
+        dv_J += p^T dout,  dp = dout V^T
+        ds = p * (dp - sum_j p_j dp_j)             (the softmax Jacobian applied to dp)
+        dq = ds K * scale, dk_J += ds^T q * scale
+
+    Rows with no kept block contribute nothing."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    dout = np.asarray(dout, np.float64)
+    B, nq, Hh, D = q.shape
+    nk = k.shape[1]
+    nbq = -(-nq // block_q)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hh):
+            base = _slab(n_slabs, b, h, Hh) * nbq
+            for i in range(nbq):
+                r = base + i
+                toks = _key_tokens(col_idx[row_ptr[r]:row_ptr[r + 1]], block_k, nk)
+                if len(toks) == 0:
+                    continue
+                q0, q1 = i * block_q, min((i + 1) * block_q, nq)
+                qi, di = q[b, q0:q1, h], dout[b, q0:q1, h]
+                kj, vj = k[b, toks, h], v[b, toks, h]
+                p = block_softmax(qi, kj, scale)
+                dv[b, toks, h] += p.T @ di
+                dp = di @ vj.T
+                ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+                dq[b, q0:q1, h] = ds @ kj * scale
+                dk[b, toks, h] += ds.T @ qi * scale
+    return dq, dk, dv
