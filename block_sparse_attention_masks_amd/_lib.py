@@ -38,6 +38,8 @@ _SIGS = {
     "vsa_mask_sta_heads": ([_I32] * 6 + [_P, _I32, _I64, _P, _P, _I64, _P], _I32),
     "vsa_mask_union": ([_I64, _I32, _P, _P, _I64, _P, _P, _I64, _P, _P, _I64, _P], _I32),
     "vsa_block_sics": ([_P, _I32, _I64, _I32, _I32, _I64, _I32, _P, _P], _I32),
+    "vsa_block_sparse_attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I64, _I64, _I32,
+                                   _I32, _P, _P, _I32, _F32, _P, ctypes.POINTER(ctypes.c_size_t), _P], _I32),
     "vsa_kv_plan": ([_P, _P, _I64, _I64, _I64, _I32, _P, _P, _P], _I32),
     "vsa_kv_gather": ([_P, _I32, _I64, _I32, _I32, _I64, _I32, _P, _I64, _P, _I64, _P], _I32),
     "vsa_mask_remap": ([_P, _P, _I64, _I64, _P, _I32, _P, _P], _I32),
@@ -282,6 +284,40 @@ def vsa_kv_compact(k, v, row_ptr, col_idx, n_slabs, block_q, block_k):
     vc = vsa_kv_gather(v, slot, n_slabs, block_k, n_out)
     cc = vsa_mask_remap(row_ptr, col_idx, n_slabs, nq_blocks, slot, -(-nk // block_k))
     return kc, vc, cc, n_out, slot, info
+
+
+def vsa_block_sparse_attn_bwd(q, k, v, o, dout, lse, row_ptr, col_idx, block_q, block_k, n_slabs=1, scale=None,
+                              dq=None, dk=None, dv=None, workspace=None):
+    """Gradients (dq, dk, dv) fp32 of L = sum(dout * o) for o = vsa_block_sparse_attn_fwd(q, k, v) with the
+    same mask; o and lse are the forward's outputs.  The workspace is allocated if not given."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (lse, "lse"), (row_ptr, "row_ptr"),
+                  (col_idx, "col_idx")):
+        _require(t, nm, q.device)
+    if q.dtype not in _DTYPE or any(t.dtype != q.dtype for t in (k, v, o, dout)):
+        raise ValueError("q, k, v, o, dout must share one dtype (float32 or bfloat16)")
+    if lse.dtype != torch.float32:
+        raise ValueError("lse must be float32")
+    B, nq, H, D = q.shape
+    nk = k.shape[1]
+    scale = D ** -0.5 if scale is None else scale
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device) if dv is None else dv
+    for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _require(t, nm, q.device)
+        if t.dtype != torch.float32:
+            raise ValueError(f"{nm} must be float32")
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+            _DTYPE[q.dtype], B, H, D, nq, nk, block_q, block_k, _ptr(row_ptr), _ptr(col_idx), n_slabs, scale)
+    need = ctypes.c_size_t(0)
+    _check(lib().vsa_block_sparse_attn_bwd(*args, None, ctypes.byref(need), _stream(q)), "vsa_block_sparse_attn_bwd")
+    if workspace is None:
+        workspace = torch.empty(max(1, need.value), dtype=torch.uint8, device=q.device)
+    _require(workspace, "workspace", q.device)
+    nb = ctypes.c_size_t(workspace.numel())
+    _check(lib().vsa_block_sparse_attn_bwd(*args, _ptr(workspace), ctypes.byref(nb), _stream(q)),
+           "vsa_block_sparse_attn_bwd")
+    return dq, dk, dv
 
 
 def _select(threshold, topk, forced):

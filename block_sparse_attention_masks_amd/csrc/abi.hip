@@ -248,4 +248,33 @@ vsa_status vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v
   return from_hip(vsa::launch_attn_fwd(a, stream));
 }
 
+vsa_status vsa_block_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                     const void* dout, const float* lse, float* dq, float* dk, float* dv,
+                                     int32_t dtype, int64_t batch, int32_t heads, int32_t head_dim, int64_t nq,
+                                     int64_t nk, int32_t block_q, int32_t block_k, const int32_t* row_ptr,
+                                     const int32_t* col_idx, int32_t n_slabs, float scale, void* workspace,
+                                     size_t* workspace_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !row_ptr || !col_idx) return VSA_ERR_NULL;
+  vsa_status st = check_tokens(dtype, batch, heads, head_dim, nq, nk, block_q, block_k);
+  if (st != VSA_OK) return st;
+  if (n_slabs != 1 && (int64_t)n_slabs != batch * heads) return VSA_ERR_PARAM;
+  if (!(scale > 0.0f) || scale == INFINITY) return VSA_ERR_PARAM;
+  const int64_t nbq = ceil_div(nq, block_q), nbk = ceil_div(nk, block_k);
+  if ((int64_t)n_slabs * nbq * nbk > kI32Max || batch * heads * nq > kI32Max) return VSA_ERR_SHAPE;
+  vsa::AttnBwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, dtype, batch, heads, head_dim, nq, nk, block_q, block_k,
+                     row_ptr, col_idx, n_slabs, scale};
+  const size_t need = vsa::attn_bwd_workspace(a);
+  if (!workspace) {
+    if (!workspace_bytes) return VSA_ERR_NULL;
+    *workspace_bytes = need;  // size query
+    return VSA_OK;
+  }
+  if (!workspace_bytes || *workspace_bytes < need) return VSA_ERR_CAPACITY;
+  if (!dq || !dk || !dv) return VSA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || ((uintptr_t)workspace & 255u))
+    return VSA_ERR_UNSUPPORTED;
+  return from_hip(vsa::launch_attn_bwd(a, workspace, stream));
+}
+
 }  // extern "C"

@@ -111,4 +111,20 @@ struct AttnArgs {
 };
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);
 
+struct AttnBwdArgs {
+  const void *q, *k, *v, *o, *dout;
+  const float* lse;
+  float *dq, *dk, *dv;
+  int dtype;
+  int64_t batch;
+  int heads, head_dim;
+  int64_t nq, nk;
+  int block_q, block_k;
+  const int32_t *row_ptr, *col_idx;
+  int n_slabs;
+  float scale;
+};
+size_t attn_bwd_workspace(const AttnBwdArgs& a);
+hipError_t launch_attn_bwd(const AttnBwdArgs& a, void* workspace, hipStream_t stream);
+
 }  // namespace vsa

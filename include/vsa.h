@@ -6,7 +6,7 @@
  * CSR list of kept key blocks (vsa_mask_sta, vsa_mask_radial, vsa_mask_nabla; composed
  * with vsa_mask_sta_heads and vsa_mask_union),
  * then compute exact softmax(Q K^T * scale) V over the kept blocks only
- * (vsa_block_sparse_attn_fwd).
+ * (vsa_block_sparse_attn_fwd) and its gradients (vsa_block_sparse_attn_bwd).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -299,6 +299,39 @@ vsa_status vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v
                                      const int32_t* row_ptr, const int32_t* col_idx,
                                      int32_t n_slabs, float scale,
                                      void* workspace, size_t* workspace_bytes,
+                                     hipStream_t stream);
+
+/*
+ * vsa_block_sparse_attn_bwd -- gradients of the forward above.
+ *
+ * Radial Attention explainer (aibr.jp/archives/112136), sec. 4: the sparse
+ * pattern saves training as well as inference time, so the path has a backward
+ * pass.  For L = sum(dout * o) with o = vsa_block_sparse_attn_fwd(q, k, v) over
+ * the same mask, with p = exp(q . k * scale - lse) and D_i = sum_d dout_i o_i:
+ *   dv_j = sum_i p_ij dout_i,  dp_ij = dout_i . v_j,  ds_ij = p_ij (dp_ij - D_i),
+ *   dq_i = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,
+ * sums over the kept (query, key) pairs only.  bf16 inputs run on the matrix
+ * cores with p and ds rounded to bf16; fp32 inputs stay fp32.  The result is
+ * deterministic (no atomics): key gradients walk a transposed copy of the mask.
+ *
+ * q, o, dout [batch, nq, heads, head_dim]; k, v [batch, nk, heads, head_dim];
+ *          device, dtype, 16-byte aligned; o and lse as written by the forward.
+ * dq, dk, dv  device fp32 outputs with the shapes of q, k, v, 16-byte aligned;
+ *          rows no kept pair touches get 0.
+ * row_ptr/col_idx, n_slabs, scale: as for the forward.
+ * workspace: device, 256-byte aligned; call with workspace = NULL to get the
+ *          size in *workspace_bytes (fp32 D per query, and the transposed mask
+ *          sized for n_slabs * n_qblocks * n_kblocks entries).
+ * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE, VSA_ERR_DTYPE, VSA_ERR_PARAM (n_slabs,
+ * scale), VSA_ERR_UNSUPPORTED (head_dim, alignment), VSA_ERR_CAPACITY
+ * (workspace_bytes smaller than the query), VSA_ERR_HIP.
+ */
+vsa_status vsa_block_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                     const void* dout, const float* lse, float* dq, float* dk, float* dv,
+                                     int32_t dtype, int64_t batch, int32_t heads, int32_t head_dim,
+                                     int64_t nq, int64_t nk, int32_t block_q, int32_t block_k,
+                                     const int32_t* row_ptr, const int32_t* col_idx, int32_t n_slabs,
+                                     float scale, void* workspace, size_t* workspace_bytes,
                                      hipStream_t stream);
 
 #ifdef __cplusplus

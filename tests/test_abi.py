@@ -209,3 +209,26 @@ def test_kv_validation(L):
     assert g(out=ODD) == E_UNSUP
     assert L.vsa_mask_remap(FAKE, FAKE, 1, 4, NULL, 16, FAKE, NULL) == E_NULL
     assert L.vsa_mask_remap(FAKE, FAKE, 1, 0, FAKE, 16, FAKE, NULL) == E_SHAPE
+
+
+def bwd(L, q=FAKE, dtype=1, D=128, slabs=1, scale=0.1, ws=FAKE, nbytes=10 ** 9, dq=FAKE, query=False):
+    nb = ctypes.c_size_t(nbytes)
+    st = L.vsa_block_sparse_attn_bwd(q, FAKE, FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE, dtype, 1, 2, D, 100, 90,
+                                     64, 64, FAKE, FAKE, slabs, scale, NULL if query else ws, ctypes.byref(nb), NULL)
+    return st, nb.value
+
+
+def test_bwd_validation(L):
+    assert bwd(L, q=NULL)[0] == E_NULL
+    assert bwd(L, dtype=9)[0] == E_DTYPE
+    assert bwd(L, D=48)[0] == E_UNSUP
+    assert bwd(L, slabs=3)[0] == E_PARAM
+    assert bwd(L, scale=0.0)[0] == E_PARAM
+    st, need = bwd(L, query=True)
+    assert st == OK
+    # D per query, CSC counters and pointers, query-block indices (dense bound), 256-byte aligned
+    expect = sum(-(-x // 256) * 256 for x in (4 * 2 * 100, 4 * 2, 4 * 3, 4 * 2 * 2))
+    assert need == expect
+    assert bwd(L, nbytes=need - 1)[0] == E_CAP
+    assert bwd(L, dq=NULL)[0] == E_NULL
+    assert bwd(L, dq=ODD)[0] == E_UNSUP

@@ -249,3 +249,54 @@ def test_kv_compaction_matches_oracle(B, H, D, nq, nk, bq, bk, slabs, dtype, tai
     o_full, l_full = vsa.vsa_block_sparse_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), rpd, cid, bq, bk, slabs)
     o_comp, l_comp = vsa.vsa_block_sparse_attn_fwd(q.to(DEV), kc, vc, rpd, cc, bq, bk, slabs)
     assert torch.equal(o_full, o_comp) and torch.equal(l_full, l_comp)
+
+
+# -------------------------------------------------------------- backward
+BWD_CASES = [
+    # nq, nk, heads, D, bq, bk, density, slabs, dtype
+    (256, 256, 2, 128, 64, 64, 1.0, 1, torch.bfloat16),          # dense; key split in both kernels
+    (1000, 937, 3, 128, 128, 128, 0.4, 3, torch.bfloat16),       # ragged tails
+    (777, 1234, 2, 128, 384, 384, 0.6, 2, torch.bfloat16),       # large blocks, several tiles per block
+    (500, 900, 2, 64, 100, 70, 0.5, 2, torch.bfloat16),          # D = 64, blocks not multiples of 64
+    (130, 700, 1, 128, 64, 48, 0.3, 1, torch.bfloat16),          # nq != nk
+    (300, 300, 2, 64, 64, 64, 0.5, 2, torch.float32),
+    (200, 333, 2, 128, 32, 48, 0.5, 1, torch.float32),
+]
+# Normalised error bounds: |g - ref| over the reference's max (and mean) magnitude.  bf16:
+# P and dS are rounded to bf16 before the products (relative 2^-9 each) and D = sum dO * O
+# uses the forward's bf16 output, so each summed term carries ~2^-9 = 1.95e-3 relative
+# error; the mean error is ~2^-9 of the mean magnitude and no element may exceed 8x that
+# of the largest.  fp32: the same sums in fp32 (~1e-6 measured).
+BWD_BF16_MAX, BWD_BF16_MEAN, BWD_F32_MAX = 8 * 2.0 ** -9, 2 * 2.0 ** -9, 1e-5
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[str(i) for i in range(len(BWD_CASES))])
+def test_attention_backward_parity(case):
+    nq, nk, H, D, bq, bk, dens, slabs, dtype = case
+    scale = D ** -0.5
+    q, k, v = rand((1, nq, H, D), dtype, 60), rand((1, nk, H, D), dtype, 61), rand((1, nk, H, D), dtype, 62)
+    do = rand((1, nq, H, D), dtype, 63)
+    nbq, nbk = -(-nq // bq), -(-nk // bk)
+    rng = np.random.default_rng(64)
+    keep = rng.random((slabs * nbq, nbk)) < dens
+    keep[np.arange(slabs * nbq), rng.integers(0, nbk, size=slabs * nbq)] = True
+    if slabs * nbq > 2:
+        keep[1] = False                                           # an empty row
+    rp, ci = oracle.csr_from_bool(keep)
+    rpd, cid = torch.from_numpy(rp).to(DEV), torch.from_numpy(ci).to(DEV)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = vsa.vsa_block_sparse_attn_fwd(qd, kd, vd, rpd, cid, bq, bk, slabs, scale)
+    dq, dk, dv = vsa.vsa_block_sparse_attn_bwd(qd, kd, vd, o, dod, lse, rpd, cid, bq, bk, slabs, scale)
+    rq, rk, rv = oracle.attention_bwd(to_np(q), to_np(k), to_np(v), to_np(do), rp, ci, bq, bk, scale, slabs)
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        g = got.cpu().double().numpy()
+        err = np.abs(g - ref)
+        mx, mn = err.max() / np.abs(ref).max(), err.mean() / np.abs(ref).mean()
+        print(f"bwd case {case[:8]} {name}: max_norm {mx:.2e} mean_norm {mn:.2e}", flush=True)
+        if dtype == torch.float32:
+            assert mx <= BWD_F32_MAX, name
+        else:
+            assert mx <= BWD_BF16_MAX and mn <= BWD_BF16_MEAN, name
+    # rows of the empty query block get exactly zero dq
+    if slabs * nbq > 2:
+        assert torch.all(dq[0, bq:min(2 * bq, nq), 0] == 0)
