@@ -241,6 +241,7 @@ def main():
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the path shards by head "
@@ -312,6 +313,34 @@ def main():
                  "speedup_vs_dense": float(np.mean(dms)) / attn_ms}
         print(f"[bench] dense run {dense['ms']:.2f} ms ({dense['tflops']:.1f} TFLOP/s)", file=sys.stderr, flush=True)
 
+    # Backward over the same mask (gradients of sum(dO * O)), timed on its own after the
+    # forward, with a seeded dO.  FLOPs are counted as 2.5x the forward's kept-block FLOPs
+    # (the five products S, dP, dV, dQ, dK); recomputing S and dP in both kernels is not counted.
+    bwd = None
+    if not args.no_bwd:
+        kx, vx, cx = ((path.kc, path.vc, path.cc) if path.compact is not None else (path.ka, path.va, path.ci))
+        gd = torch.Generator(device=dev).manual_seed(7)
+        dout = torch.randn(path.oa.shape, generator=gd, device=dev).to(path.oa.dtype)
+        path.attn()
+        dq_, dk_, dv_ = (torch.empty(t.shape, dtype=torch.float32, device=dev) for t in (path.qa, kx, vx))
+        bargs = (path.qa, kx, vx, path.oa, dout, path.lse, path.rp, cx, path.bq, path.bk, path.n_slabs, path.scale)
+        wsb = torch.empty(max(1, path.vsa.attn_bwd_workspace_bytes(*bargs)), dtype=torch.uint8, device=dev)
+        bms = []
+        for rep_ in range(4):                                  # the first call is a warm-up
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            path.vsa.vsa_block_sparse_attn_bwd(*bargs, dq=dq_, dk=dk_, dv=dv_, workspace=wsb)
+            b.record(stream)
+            b.synchronize()
+            if rep_:
+                bms.append(a.elapsed_time(b))
+        bwd_ms = float(np.mean(bms))
+        bwd = {"ms": round(bwd_ms, 4), "tflops": round(2.5 * flops / (bwd_ms * 1e-3) / 1e12, 2),
+               "pct_bf16_peak": round(100 * 2.5 * flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+               "flops_counted": 2.5 * flops, "outputs": "dq, dk, dv fp32"}
+        print(f"[bench] backward {bwd_ms:.3f} ms ({bwd['tflops']:.1f} TFLOP/s at 2.5x forward FLOPs)",
+              file=sys.stderr, flush=True)
+
     # SICS block scores (SPADE's scheme-step score) of the attention-order K, timed on their
     # own, outside the step: HBM-bound, reported against the HBM peak and as a fraction of
     # the attention time.
@@ -378,6 +407,7 @@ def main():
         "dense_tflops": None if dense is None else round(dense["tflops"], 2),
         "stage_ms": {k_: round(float(np.mean(v_)), 4) for k_, v_ in ev.items()},
         "sics": sics,
+        "backward": bwd,
         "kv_compaction": (None if path.compact is None else
                           {"tokens_before": path.nk, "tokens_after": path.n_out,
                            "reduction": round(1 - path.n_out / path.nk, 4),

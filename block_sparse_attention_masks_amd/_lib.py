@@ -286,6 +286,18 @@ def vsa_kv_compact(k, v, row_ptr, col_idx, n_slabs, block_q, block_k):
     return kc, vc, cc, n_out, slot, info
 
 
+def attn_bwd_workspace_bytes(q, k, v, o, dout, lse, row_ptr, col_idx, block_q, block_k, n_slabs=1, scale=None):
+    """Workspace bytes vsa_block_sparse_attn_bwd needs for these arguments (no launch)."""
+    B, nq, H, D = q.shape
+    scale = D ** -0.5 if scale is None else scale
+    need = ctypes.c_size_t(0)
+    _check(lib().vsa_block_sparse_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), None, None,
+                                           None, _DTYPE[q.dtype], B, H, D, nq, k.shape[1], block_q, block_k,
+                                           _ptr(row_ptr), _ptr(col_idx), n_slabs, scale, None, ctypes.byref(need),
+                                           _stream(q)), "vsa_block_sparse_attn_bwd")
+    return need.value
+
+
 def vsa_block_sparse_attn_bwd(q, k, v, o, dout, lse, row_ptr, col_idx, block_q, block_k, n_slabs=1, scale=None,
                               dq=None, dk=None, dv=None, workspace=None):
     """Gradients (dq, dk, dv) fp32 of L = sum(dout * o) for o = vsa_block_sparse_attn_fwd(q, k, v) with the

@@ -36,6 +36,8 @@ from .masks import (  # noqa: F401
     pool_blocks, nabla_select_row, mask_nabla, ar_forced_ranges, ar_select_row, mask_ar,
     mask_sta_heads, mask_union, csr_concat,
 )
-from .attention import attention, attention_bwd, attention_rows, block_softmax  # noqa: F401
+from .attention import (  # noqa: F401
+    attention, attention_bwd, attention_bwd_key_block, attention_bwd_query_rows, attention_rows, block_softmax,
+)
 from .sics import block_sics  # noqa: F401
 from . import kvcache  # noqa: F401

@@ -140,3 +140,48 @@ def attention_bwd(q, k, v, dout, row_ptr, col_idx, block_q, block_k, scale, n_sl
                 dq[b, q0:q1, h] = ds @ kj * scale
                 dk[b, toks, h] += ds.T @ qi * scale
     return dq, dk, dv
+
+
+def attention_bwd_query_rows(q_rows, row_tokens, dout_rows, kh, vh, row_ptr, col_idx, row_base, block_q, block_k,
+                             scale):
+    """dq of selected query rows of one (batch, head), by the same steps as attention_bwd.
+
+    q_rows, dout_rows [n, D]; row_tokens [n] = their query positions; kh, vh [Nk, D].
+    The CSR row of position t is row_base + t // block_q."""
+    nk = kh.shape[0]
+    out = np.zeros((len(row_tokens), kh.shape[1]))
+    for n, t in enumerate(row_tokens):
+        r = row_base + t // block_q
+        toks = _key_tokens(col_idx[row_ptr[r]:row_ptr[r + 1]], block_k, nk)
+        if len(toks) == 0:
+            continue
+        kj, vj = kh[toks], vh[toks]
+        p = block_softmax(q_rows[n][None], kj, scale)[0]
+        dp = vj @ dout_rows[n]
+        ds = p * (dp - (p * dp).sum())
+        out[n] = ds @ kj * scale
+    return out
+
+
+def attention_bwd_key_block(j, qh, kh, vh, douth, row_ptr, col_idx, row_base, n_qblocks, block_q, block_k, scale):
+    """(dk, dv) of the tokens of key block j of one (batch, head): the sums of attention_bwd
+    over every query block whose row keeps j.  qh, douth [Nq, D]; kh, vh [Nk, D]."""
+    nq, nk = qh.shape[0], kh.shape[0]
+    j0, j1 = j * block_k, min((j + 1) * block_k, nk)
+    dk = np.zeros((j1 - j0, kh.shape[1]))
+    dv = np.zeros_like(dk)
+    for i in range(n_qblocks):
+        r = row_base + i
+        cols = col_idx[row_ptr[r]:row_ptr[r + 1]]
+        if j not in set(np.asarray(cols).tolist()):
+            continue
+        toks = _key_tokens(cols, block_k, nk)
+        q0, q1 = i * block_q, min((i + 1) * block_q, nq)
+        qi, di = qh[q0:q1], douth[q0:q1]
+        p = block_softmax(qi, kh[toks], scale)
+        dp = di @ vh[toks].T
+        ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+        sel = (toks >= j0) & (toks < j1)
+        dv += p[:, sel].T @ di
+        dk += ds[:, sel].T @ qi * scale
+    return dk, dv

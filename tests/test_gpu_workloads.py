@@ -309,3 +309,59 @@ def test_ar_kv_compaction_workload():
     o_full, l_full = vsa.vsa_block_sparse_attn_fwd(q, k, v, rp, ci, block, block, H, scale)
     o_comp, l_comp = vsa.vsa_block_sparse_attn_fwd(q, kc, vc, rp, cc, block, block, H, scale)
     assert torch.equal(o_full, o_comp) and torch.equal(l_full, l_comp)
+
+
+# ------------------------------------------------------------------ backward
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_backward_sta_workload():
+    """Gradients at the sta workload's full size (tile order, as the path runs): dq on 512
+    sampled (head, query) rows and dk, dv on 3 sampled (head, key block) pairs, each
+    from the oracle's own sampled evaluation."""
+    cfg = CONFIGS["sta"]
+    grid, tile, window = cfg["grid"], cfg["tile"], cfg["window"]
+    H, D, blk = cfg["heads"], cfg["head_dim"], 384
+    scale = D ** -0.5
+    t0 = time.time()
+    x = gen.make_inputs("sta")
+    perm = oracle.tile_order_source(grid, tile)
+    qt, kt, vt = (x[w][:, perm].contiguous() for w in ("q", "k", "v"))
+    dout = (torch.randn(qt.shape, generator=torch.Generator().manual_seed(77), dtype=torch.float32)
+            .to(torch.bfloat16))
+    qd, kd, vd, dd = (t.to(DEV) for t in (qt, kt, vt, dout))
+    rp_d, ci_d = vsa.vsa_mask_sta(grid, tile, window, DEV)
+    o, lse = vsa.vsa_block_sparse_attn_fwd(qd, kd, vd, rp_d, ci_d, blk, blk, 1, scale)
+    dq, dk, dv = vsa.vsa_block_sparse_attn_bwd(qd, kd, vd, o, dd, lse, rp_d, ci_d, blk, blk, 1, scale)
+    torch.cuda.synchronize()
+    rp, ci = csr_np(rp_d, ci_d)
+    log(f"sta bwd: GPU done {time.time() - t0:.1f}s")
+    rng = np.random.default_rng(78)
+    nq = qt.shape[1]
+    heads = rng.choice(H, 4, replace=False)
+    errs = {"dq": [], "dk": [], "dv": []}
+    refs = {"dq": [], "dk": [], "dv": []}
+    for h in heads:
+        qh, kh, vh, dh = (t[0, :, h].double().numpy() for t in (qt, kt, vt, dout))
+        rows = np.sort(rng.choice(nq, 128, replace=False))
+        ref = oracle.attention_bwd_query_rows(qh[rows], rows, dh[rows], kh, vh, rp, ci, 0, blk, blk, scale)
+        errs["dq"].append(np.abs(dq[0, rows, h].cpu().double().numpy() - ref))
+        refs["dq"].append(np.abs(ref))
+    for h, j in zip(heads[:3], rng.choice(300, 3, replace=False)):
+        qh, kh, vh, dh = (t[0, :, h].double().numpy() for t in (qt, kt, vt, dout))
+        rk, rv = oracle.attention_bwd_key_block(j, qh, kh, vh, dh, rp, ci, 0, 300, blk, blk, scale)
+        sl = slice(j * blk, (j + 1) * blk)
+        errs["dk"].append(np.abs(dk[0, sl, h].cpu().double().numpy() - rk))
+        errs["dv"].append(np.abs(dv[0, sl, h].cpu().double().numpy() - rv))
+        refs["dk"].append(np.abs(rk))
+        refs["dv"].append(np.abs(rv))
+    for name in ("dq", "dk", "dv"):
+        e, r = np.concatenate(errs[name]), np.concatenate(refs[name])
+        mx, mn = e.max() / r.max(), e.mean() / r.mean()
+        log(f"sta bwd {name}: max_norm {mx:.2e} mean_norm {mn:.2e}")
+        # As for the small cases (P, dS rounded to bf16: 2^-9 per term), except that here D
+        # = sum dO * O is built from the forward's bf16 O and enters dS un-cancelled while dq
+        # is a difference of near-equal terms: the positional code (|P|^2 = 144) makes the keys
+        # large and attention peaked, which amplifies that rounding relative to |dq| (x2.5
+        # measured), so the mean bound is 4 * 2^-9.
+        assert mx <= 8 * 2.0 ** -9 and mn <= 4 * 2.0 ** -9, name
+    log(f"sta bwd: done {time.time() - t0:.1f}s")

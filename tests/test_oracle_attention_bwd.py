@@ -80,3 +80,20 @@ def test_invariants():
     dq2, _, _ = oracle.attention_bwd(q, k + c, v, dout, rp, ci, bq, bk, scale, slabs)
     assert np.allclose(dq2, dq, atol=1e-10)
     assert np.all(dq[0, 6:12, 0] == 0)                  # query block 1 of head 0 keeps nothing
+
+
+def test_sampled_rows_and_key_blocks_match_full():
+    q, k, v, dout, rp, ci, bq, bk, slabs, _ = problem(4, B=1, H=2, D=8, nq=40, nk=33, bq=8, bk=5, slabs=2)
+    scale = 0.4
+    dq, dk, dv = oracle.attention_bwd(q, k, v, dout, rp, ci, bq, bk, scale, slabs)
+    nbq = 5
+    for h in range(2):
+        rows = np.array([0, 7, 8, 15, 39])
+        got = oracle.attention_bwd_query_rows(q[0, rows, h], rows, dout[0, rows, h], k[0, :, h], v[0, :, h],
+                                              rp, ci, h * nbq, bq, bk, scale)
+        assert np.allclose(got, dq[0, rows, h], atol=1e-12)
+        for j in range(7):
+            gk, gv = oracle.attention_bwd_key_block(j, q[0, :, h], k[0, :, h], v[0, :, h], dout[0, :, h], rp, ci,
+                                                    h * nbq, nbq, bq, bk, scale)
+            assert np.allclose(gk, dk[0, 5 * j:min(33, 5 * j + 5), h], atol=1e-12)
+            assert np.allclose(gv, dv[0, 5 * j:min(33, 5 * j + 5), h], atol=1e-12)
