@@ -188,6 +188,10 @@ class Path:
                                                        workspace=ws, row_ptr=self.rp, col_idx=self.ci,
                                                        **sel)
         self.ci = torch.empty(cap, dtype=torch.int32, device=dev)
+        # workspace of the forward (union lists when small query blocks run grouped), sized
+        # once: the step allocates nothing
+        nws = vsa.attn_fwd_workspace_bytes(self.qa, self.ka, self.rp, self.ci, self.bq, self.bk, self.n_slabs)
+        self.ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
         self.compact = None
         if name == "ar_compact":
             # size the compact cache once (the inputs are fixed); the step itself allocates nothing
@@ -217,15 +221,17 @@ class Path:
             for src, dst in ((self.q, self.qa), (self.k, self.ka), (self.v, self.va)):
                 self.vsa.vsa_tile_reorder(src, *self.tiled, out=dst)
 
-    def attn(self, rp=None, ci=None):
+    def attn(self, rp=None, ci=None, ws=None):
         if rp is None and self.compact is not None:   # over the compact cache
             self.vsa.vsa_block_sparse_attn_fwd(self.qa, self.kc, self.vc, self.rp, self.cc, self.bq, self.bk,
-                                               self.n_slabs, self.scale, out=self.oa, lse=self.lse)
+                                               self.n_slabs, self.scale, out=self.oa, lse=self.lse,
+                                               workspace=self.ws, grouped=self.ws is not None)
             return
+        wsx = self.ws if rp is None else ws
         self.vsa.vsa_block_sparse_attn_fwd(self.qa, self.ka, self.va, self.rp if rp is None else rp,
                                            self.ci if ci is None else ci, self.bq, self.bk,
                                            self.n_slabs if rp is None else 1, self.scale,
-                                           out=self.oa, lse=self.lse)
+                                           out=self.oa, lse=self.lse, workspace=wsx, grouped=wsx is not None)
 
     def reorder_out(self):
         if self.tiled:
@@ -299,12 +305,14 @@ def main():
     dense = None
     if not args.no_dense:
         drp, dci = path.vsa.all_ones_mask(path.nbq, path.nbk, dev)
-        path.attn(drp, dci)
+        nwd = path.vsa.attn_fwd_workspace_bytes(path.qa, path.ka, drp, dci, path.bq, path.bk, 1)
+        dws = torch.empty(nwd, dtype=torch.uint8, device=dev) if nwd else None
+        path.attn(drp, dci, dws)
         dms = []
         for _ in range(args.dense_reps):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            path.attn(drp, dci)
+            path.attn(drp, dci, dws)
             b.record(stream)
             b.synchronize()
             dms.append(a.elapsed_time(b))

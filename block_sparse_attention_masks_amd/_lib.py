@@ -385,8 +385,12 @@ def vsa_mask_nabla(q, k, block_q, block_k, scale=None, threshold=None, topk=0, f
 
 
 def vsa_block_sparse_attn_fwd(q, k, v, row_ptr, col_idx, block_q, block_k, n_slabs=1, scale=None,
-                              out=None, lse=None, want_lse=True):
-    """Exact softmax attention over the kept blocks -> (o, lse or None)."""
+                              out=None, lse=None, want_lse=True, workspace=None, grouped=True):
+    """Exact softmax attention over the kept blocks -> (o, lse or None).
+
+    Small query blocks run grouped (several blocks per workgroup over the union of their
+    kept blocks) when a workspace is available: it is allocated here unless given, and
+    grouped=False runs without one (same results, bit for bit)."""
     for name, t in (("q", q), ("k", k), ("v", v), ("row_ptr", row_ptr), ("col_idx", col_idx)):
         _require(t, name, q.device)
     B, nq, Hh, D = q.shape
@@ -402,11 +406,34 @@ def vsa_block_sparse_attn_fwd(q, k, v, row_ptr, col_idx, block_q, block_k, n_sla
     _require(out, "out", q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hh, nq), dtype=torch.float32, device=q.device)
-    _check(lib().vsa_block_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                                           _DTYPE[q.dtype], B, Hh, D, nq, nk, block_q, block_k,
-                                           _ptr(row_ptr), _ptr(col_idx), n_slabs, float(scale),
-                                           None, None, _stream(q)), "vsa_block_sparse_attn_fwd")
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _DTYPE[q.dtype], B, Hh, D, nq, nk, block_q, block_k,
+            _ptr(row_ptr), _ptr(col_idx), n_slabs, float(scale))
+    nb = ctypes.c_size_t(0)
+    if grouped:
+        if workspace is None:
+            _check(lib().vsa_block_sparse_attn_fwd(*args, None, ctypes.byref(nb), _stream(q)),
+                   "vsa_block_sparse_attn_fwd")
+            if nb.value:
+                workspace = torch.empty(nb.value, dtype=torch.uint8, device=q.device)
+        if workspace is not None:
+            _require(workspace, "workspace", q.device)
+            nb = ctypes.c_size_t(workspace.numel())
+    else:
+        workspace = None
+    _check(lib().vsa_block_sparse_attn_fwd(*args, _ptr(workspace) if workspace is not None else None,
+                                           ctypes.byref(nb) if workspace is not None else None, _stream(q)),
+           "vsa_block_sparse_attn_fwd")
     return out, lse
+
+
+def attn_fwd_workspace_bytes(q, k, row_ptr, col_idx, block_q, block_k, n_slabs=1):
+    """Workspace bytes the forward uses to group small query blocks (0: none)."""
+    B, nq, Hh, D = q.shape
+    nb = ctypes.c_size_t(0)
+    _check(lib().vsa_block_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(k), _ptr(q), None, _DTYPE[q.dtype], B, Hh, D, nq,
+                                           k.shape[1], block_q, block_k, _ptr(row_ptr), _ptr(col_idx), n_slabs,
+                                           D ** -0.5, None, ctypes.byref(nb), _stream(q)), "vsa_block_sparse_attn_fwd")
+    return nb.value
 
 
 def all_ones_mask(n_qblocks, n_kblocks, device):

@@ -232,20 +232,22 @@ vsa_status vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v
                                      const int32_t* col_idx, int32_t n_slabs, float scale,
                                      void* workspace, size_t* workspace_bytes,
                                      hipStream_t stream) {
-  (void)workspace;
   if (!q || !k || !v || !o || !row_ptr || !col_idx) return VSA_ERR_NULL;
   vsa_status st = check_tokens(dtype, batch, heads, head_dim, nq, nk, block_q, block_k);
   if (st != VSA_OK) return st;
   if (n_slabs != 1 && (int64_t)n_slabs != batch * heads) return VSA_ERR_PARAM;
   if (!(scale > 0.0f) || scale == INFINITY) return VSA_ERR_PARAM;
-  if (workspace_bytes && !workspace) {  // size query: no workspace needed
-    *workspace_bytes = 0;
+  vsa::AttnArgs a{q, k, v, o, lse, dtype, batch, heads, head_dim, nq, nk, block_q, block_k,
+                  row_ptr, col_idx, n_slabs, scale};
+  const size_t want = dtype == VSA_BF16 ? vsa::attn_fwd_workspace(a) : 0;
+  if (workspace_bytes && !workspace) {  // size query
+    *workspace_bytes = want;
     return VSA_OK;
   }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return VSA_ERR_UNSUPPORTED;
-  vsa::AttnArgs a{q, k, v, o, lse, dtype, batch, heads, head_dim, nq, nk, block_q, block_k,
-                  row_ptr, col_idx, n_slabs, scale};
-  return from_hip(vsa::launch_attn_fwd(a, stream));
+  if (workspace && ((uintptr_t)workspace & 255u)) return VSA_ERR_UNSUPPORTED;
+  const size_t have = workspace && workspace_bytes ? *workspace_bytes : 0;
+  return from_hip(vsa::launch_attn_fwd(a, workspace, have, stream));
 }
 
 vsa_status vsa_block_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,

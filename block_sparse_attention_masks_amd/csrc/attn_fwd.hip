@@ -55,6 +55,14 @@ struct Work {
   int nbq, mt_per_qb;
 };
 
+// Grouped query blocks: G consecutive query blocks of a slab share a workgroup of G * wpb
+// waves and walk the union of their kept key blocks.  List u = slab * n_groups + group
+// holds cnt[u] entries at col[u * cap ..], each with a mask of the rows that keep it.
+struct Groups {
+  const int32_t *col, *mask, *cnt;
+  int G, wpb, cap;
+};
+
 // Stream of 64-key tiles over the kept blocks of one CSR row (wave-uniform).
 struct TileIter {
   const int32_t* col;
@@ -175,15 +183,16 @@ struct Smem {
   uint16_t v[2][kBN * D];
 };
 
-template <int D, int KS, int NW>
+template <int D, int KS, int NW, bool GR>
 __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
     int64_t nq, int64_t nk, int heads, int block_q, int block_k,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int n_slabs,
-    float scale_log2, Work wk) {
+    float scale_log2, Work wk, Groups gp) {
   __shared__ __attribute__((aligned(1024))) Smem<D> sm;
   static_assert(KS == 1 || NW == 4, "key split runs with 4 waves");
+  static_assert(!GR || KS == 1, "grouped query blocks use whole tiles");
   constexpr int BM = 32 * NW / KS;
   constexpr int NST = 2 / KS;
   constexpr int SPR = D / 8;              // 16-byte slots per row
@@ -191,6 +200,8 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
   constexpr int CB = kBN / RPC;           // wave-loads per tensor per tile
   constexpr int NJ = (2 * CB + NW - 1) / NW;  // wave-loads per wave per tile (K and V together)
 
+  // work item: (batch, head, query block, row tile) -- or, grouped, (batch, head, group
+  // of gp.G query blocks); wk.nbq counts query blocks or groups
   const int64_t bid = blockIdx.x;
   const int64_t item = (bid % 8) * wk.per_xcd + bid / 8;
   if (item >= wk.items) return;
@@ -200,9 +211,6 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
   rest /= wk.nbq;
   const int h = (int)(rest % heads);
   const int64_t b = rest / heads;
-  const int64_t q_lo = (int64_t)qb * block_q + (int64_t)mt * BM;
-  const int64_t q_hi = min(min((int64_t)(qb + 1) * block_q, nq), q_lo + BM);
-  if (q_lo >= q_hi) return;
 
   const int tid = threadIdx.x, l = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -210,10 +218,30 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
   const int qw = KS == 1 ? w : (w & 1);
   const int kh = KS == 1 ? 0 : (w >> 1);
   const int row_stride = heads * D;
+  // this wave's 32 query rows [q_w, q_hi)
+  int64_t q_w, q_hi;
+  int lq = 0;  // grouped: the wave's query block within the group
+  if constexpr (GR) {
+    lq = w / gp.wpb;
+    const int64_t qbw = (int64_t)qb * gp.G + lq;
+    q_w = qbw * block_q + (int64_t)(w % gp.wpb) * 32;
+    q_hi = lq < gp.G ? min(min((qbw + 1) * block_q, nq), q_w + 32) : q_w;
+  } else {
+    const int64_t q_lo = (int64_t)qb * block_q + (int64_t)mt * BM;
+    if (q_lo >= min((int64_t)(qb + 1) * block_q, nq)) return;
+    q_w = q_lo + qw * 32;
+    q_hi = min(min((int64_t)(qb + 1) * block_q, nq), q_lo + BM);
+  }
 
   const int64_t slab = n_slabs == 1 ? 0 : b * heads + h;
-  const int64_t r = slab * wk.nbq + qb;
-  TileIter it{col_idx, row_ptr[r], row_ptr[r + 1], 0, 0, block_k, nk};
+  TileIter it;
+  if constexpr (GR) {  // the union of the group's kept blocks, with a row-membership mask
+    const int64_t u = slab * wk.nbq + qb;
+    it = TileIter{gp.col, (int)(u * gp.cap), (int)(u * gp.cap) + gp.cnt[u], 0, 0, block_k, nk};
+  } else {
+    const int64_t r = slab * wk.nbq + qb;
+    it = TileIter{col_idx, row_ptr[r], row_ptr[r + 1], 0, 0, block_k, nk};
+  }
   it.open();
   const uint16_t* kbase = k + (b * nk * heads + h) * (int64_t)D;
   const uint16_t* vbase = v + (b * nk * heads + h) * (int64_t)D;
@@ -248,11 +276,11 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
     }
   };
 
-  const int64_t my_q = q_lo + qw * 32 + col;
+  const int64_t my_q = q_w + col;
   bf16x8 qf[D / 16];
   {
     const bool ok = my_q < q_hi;
-    const uint16_t* qp = q + ((b * nq + (ok ? my_q : q_lo)) * heads + h) * D + 8 * g;
+    const uint16_t* qp = q + ((b * nq + (ok ? my_q : 0)) * heads + h) * D + 8 * g;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       u32x4 u = ok ? *(const u32x4*)(qp + 16 * s) : u32x4{0, 0, 0, 0};
@@ -285,6 +313,8 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
     if (nx.valid()) issue(nx.k0, nx.ke, buf ^ 1);
     const uint16_t* sk = sm.k[buf];
     const uint16_t* sv = sm.v[buf];
+    // grouped: a wave whose query block does not keep this key block only helps copy it
+    if (!GR || ((gp.mask[it.e] >> lq) & 1)) {
     f32x16 s[NST];
 #pragma unroll
     for (int st = 0; st < NST; ++st)
@@ -355,6 +385,7 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
 #pragma unroll
       for (int t = 0; t < D / 32; ++t)
         acc_o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t], pf[kk], acc_o[t], 0, 0, 0);
+    }
     }
     wait_vmcnt<0>();               // the next tile's loads have landed
     __builtin_amdgcn_s_barrier();  // ... for everyone; this tile is no longer read
@@ -455,7 +486,84 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
 
 }  // namespace
 
-hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
+namespace {
+
+// One wave per (slab, group): lane r < G walks row r of the group; each step takes the
+// smallest column any lane still holds (a wave minimum), records the lanes holding it as
+// the entry's mask, and advances them.  Lists are written at u * cap, their lengths to cnt.
+constexpr int kUnionWaves = 4;
+__global__ __launch_bounds__(kUnionWaves * kWave) void group_union_kernel(
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int nbq, int64_t n_lists, int G,
+    int n_groups, int cap, int32_t* __restrict__ gcol, int32_t* __restrict__ gmask, int32_t* __restrict__ gcnt) {
+  const int64_t u = (int64_t)blockIdx.x * kUnionWaves + threadIdx.x / kWave;
+  if (u >= n_lists) return;
+  const int l = lane_id();
+  const int64_t slab = u / n_groups;
+  const int qb = (int)(u % n_groups) * G + l;
+  int32_t e = 0, e1 = 0;
+  if (l < G && qb < nbq) {
+    e = row_ptr[slab * nbq + qb];
+    e1 = row_ptr[slab * nbq + qb + 1];
+  }
+  int32_t* oc = gcol + u * cap;
+  int32_t* om = gmask + u * cap;
+  int n = 0;
+  while (true) {
+    const int32_t val = e < e1 ? col_idx[e] : INT32_MAX;
+    int32_t m = val;
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) m = min(m, __shfl_xor(m, o, kWave));
+    if (m == INT32_MAX || n >= cap) break;  // cap: rows hold distinct columns below it
+    const uint64_t bits = __ballot(val == m);
+    if (l == 0) {
+      oc[n] = m;
+      om[n] = (int32_t)bits;
+    }
+    if (val == m) ++e;
+    ++n;
+  }
+  if (l == 0) gcnt[u] = n;
+}
+
+// How a call runs: grouped (wpb waves per query block, G blocks per workgroup of nw
+// waves), or per query block (ks = 2 key split for blocks <= 64 rows, else nw waves).
+struct FwdPlan {
+  bool grouped;
+  int ks, nw, G, wpb, n_groups;
+  size_t ws_bytes;
+};
+
+FwdPlan plan_fwd(const AttnArgs& a, bool have_ws) {
+  FwdPlan p{false, 1, 4, 1, 1, 0, 0};
+  const int64_t nbq = (a.nq + a.block_q - 1) / a.block_q, nbk = (a.nk + a.block_k - 1) / a.block_k;
+  const int wpb = (a.block_q + 31) / 32;
+  // query blocks of <= 128 rows: group them when enough workgroups remain to fill the chip
+  if (wpb <= 4) {
+    for (int nw : {12, 8, 4}) {
+      if (nw % wpb) continue;
+      const int G = nw / wpb;
+      const int64_t n_groups = (nbq + G - 1) / G;
+      const int64_t items = a.batch * a.heads * n_groups;
+      const int64_t lists = (int64_t)a.n_slabs * n_groups;
+      if (G < 2 || items < (nw == 4 ? 512 : 256) || lists * nbk > 0x7fffffff) continue;
+      p = FwdPlan{true, 1, nw, G, wpb, (int)n_groups, 0};
+      auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+      p.ws_bytes = 2 * al(4 * (size_t)(lists * nbk)) + al(4 * (size_t)lists);
+      break;
+    }
+  }
+  if (p.grouped && have_ws) return p;
+  const bool want = p.grouped;
+  p = FwdPlan{false, a.block_q <= kBM / 2 ? 2 : 1, 4, 1, 1, 0, want ? p.ws_bytes : 0};
+  if (p.ks == 1) p.nw = a.block_q % 384 == 0 ? 12 : (a.block_q % 256 == 0 ? 8 : 4);
+  return p;
+}
+
+}  // namespace
+
+size_t attn_fwd_workspace(const AttnArgs& a) { return plan_fwd(a, true).ws_bytes; }
+
+hipError_t launch_attn_fwd(const AttnArgs& a, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const int nbq = (int)((a.nq + a.block_q - 1) / a.block_q);
   if (a.dtype == 0) {
     const int64_t n = a.batch * a.heads * a.nq;
@@ -473,33 +581,56 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const float sl2 = a.scale * kLog2e;
-  // Query rows per workgroup: 64 (key split) for small blocks; else 32 rows per wave with
-  // 12 or 8 waves when the block is a multiple of 384 or 256 rows (one K/V tile copy then
-  // serves more rows), else 4 waves.
-  const int ks = a.block_q <= kBM / 2 ? 2 : 1;
-  const int nw = ks == 2 ? 4 : (a.block_q % 384 == 0 ? 12 : (a.block_q % 256 == 0 ? 8 : 4));
-  const int bm = 32 * nw / ks;
+  const FwdPlan pl = plan_fwd(a, workspace != nullptr && workspace_bytes >= plan_fwd(a, true).ws_bytes);
   Work wk;
-  wk.nbq = nbq;
-  wk.mt_per_qb = (a.block_q + bm - 1) / bm;
-  wk.items = a.batch * a.heads * (int64_t)nbq * wk.mt_per_qb;
+  Groups gp{nullptr, nullptr, nullptr, 1, 1, 0};
+  if (pl.grouped) {
+    const int nbk = (int)((a.nk + a.block_k - 1) / a.block_k);
+    const int64_t lists = (int64_t)a.n_slabs * pl.n_groups;
+    auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+    char* ws = (char*)workspace;
+    int32_t* gcol = (int32_t*)ws;
+    int32_t* gmask = (int32_t*)(ws + al(4 * (size_t)(lists * nbk)));
+    int32_t* gcnt = (int32_t*)(ws + 2 * al(4 * (size_t)(lists * nbk)));
+    hipLaunchKernelGGL(group_union_kernel, dim3((unsigned)((lists + kUnionWaves - 1) / kUnionWaves)),
+                       dim3(kUnionWaves * kWave), 0, stream, a.row_ptr, a.col_idx, nbq, lists, pl.G, pl.n_groups,
+                       nbk, gcol, gmask, gcnt);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    gp = Groups{gcol, gmask, gcnt, pl.G, pl.wpb, nbk};
+    wk.nbq = pl.n_groups;
+    wk.mt_per_qb = 1;
+  } else {
+    const int bm = 32 * pl.nw / pl.ks;
+    wk.nbq = nbq;
+    wk.mt_per_qb = (a.block_q + bm - 1) / bm;
+  }
+  wk.items = a.batch * a.heads * (int64_t)wk.nbq * wk.mt_per_qb;
   wk.per_xcd = (wk.items + 7) / 8;
   const dim3 grid((unsigned)(wk.per_xcd * 8));
   auto launch = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, dim3(nw * kWave), 0, stream, (const uint16_t*)a.q,
+    hipLaunchKernelGGL(kern, grid, dim3(pl.nw * kWave), 0, stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.nq, a.nk,
-                       a.heads, a.block_q, a.block_k, a.row_ptr, a.col_idx, a.n_slabs, sl2, wk);
+                       a.heads, a.block_q, a.block_k, a.row_ptr, a.col_idx, a.n_slabs, sl2, wk, gp);
   };
   if (a.head_dim == 64) {
-    if (ks == 2) launch(attn_fwd_bf16_kernel<64, 2, 4>);
-    else if (nw == 12) launch(attn_fwd_bf16_kernel<64, 1, 12>);
-    else if (nw == 8) launch(attn_fwd_bf16_kernel<64, 1, 8>);
-    else launch(attn_fwd_bf16_kernel<64, 1, 4>);
+    if (pl.grouped) {
+      if (pl.nw == 12) launch(attn_fwd_bf16_kernel<64, 1, 12, true>);
+      else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<64, 1, 8, true>);
+      else launch(attn_fwd_bf16_kernel<64, 1, 4, true>);
+    } else if (pl.ks == 2) launch(attn_fwd_bf16_kernel<64, 2, 4, false>);
+    else if (pl.nw == 12) launch(attn_fwd_bf16_kernel<64, 1, 12, false>);
+    else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<64, 1, 8, false>);
+    else launch(attn_fwd_bf16_kernel<64, 1, 4, false>);
   } else {
-    if (ks == 2) launch(attn_fwd_bf16_kernel<128, 2, 4>);
-    else if (nw == 12) launch(attn_fwd_bf16_kernel<128, 1, 12>);
-    else if (nw == 8) launch(attn_fwd_bf16_kernel<128, 1, 8>);
-    else launch(attn_fwd_bf16_kernel<128, 1, 4>);
+    if (pl.grouped) {
+      if (pl.nw == 12) launch(attn_fwd_bf16_kernel<128, 1, 12, true>);
+      else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<128, 1, 8, true>);
+      else launch(attn_fwd_bf16_kernel<128, 1, 4, true>);
+    } else if (pl.ks == 2) launch(attn_fwd_bf16_kernel<128, 2, 4, false>);
+    else if (pl.nw == 12) launch(attn_fwd_bf16_kernel<128, 1, 12, false>);
+    else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<128, 1, 8, false>);
+    else launch(attn_fwd_bf16_kernel<128, 1, 4, false>);
   }
   return hipGetLastError();
 }

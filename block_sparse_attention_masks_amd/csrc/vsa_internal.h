@@ -109,7 +109,10 @@ struct AttnArgs {
   int n_slabs;
   float scale;
 };
-hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);
+// Workspace the bf16 forward uses for grouped query blocks (0 if none); without it the
+// call runs ungrouped.
+size_t attn_fwd_workspace(const AttnArgs& a);
+hipError_t launch_attn_fwd(const AttnArgs& a, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 struct AttnBwdArgs {
   const void *q, *k, *v, *o, *dout;

@@ -285,8 +285,13 @@ vsa_status vsa_mask_nabla(const void* q, const void* k, int32_t dtype,
  * dtype, 16-byte aligned.  lse: NULL or device [batch, heads, nq] fp32.
  * row_ptr/col_idx: CSR with n_slabs = 1 (shared) or batch*heads slabs.
  * scale: finite and > 0 (the usual 1/sqrt(head_dim)).
- * workspace / workspace_bytes as for vsa_mask_nabla (the current kernels need
- * none: the query returns 0 and NULL is accepted).
+ * workspace / workspace_bytes: call with workspace = NULL and workspace_bytes set
+ * to get the size.  bf16 query blocks of at most 128 rows are then run grouped:
+ * several consecutive query blocks share a workgroup and walk the union of their
+ * kept key blocks, so one copy of a key tile serves more query rows.  The
+ * workspace (device, 256-byte aligned) holds those union lists; with workspace =
+ * NULL, or smaller than the query, the call runs ungrouped.  Both give the same
+ * result bit for bit.
  * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE, VSA_ERR_DTYPE, VSA_ERR_PARAM (n_slabs, scale),
  * VSA_ERR_UNSUPPORTED (head_dim not 64/128, misalignment), VSA_ERR_CAPACITY,
  * VSA_ERR_HIP.  The CSR contents are trusted: column indices must lie in

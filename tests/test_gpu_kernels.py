@@ -300,3 +300,47 @@ def test_attention_backward_parity(case):
     # rows of the empty query block get exactly zero dq
     if slabs * nbq > 2:
         assert torch.all(dq[0, bq:min(2 * bq, nq), 0] == 0)
+
+
+# ------------------------------------------------- grouped small query blocks
+GROUPED_CASES = [
+    # batch, heads, D, nq, nk, bq, bk, density, per-head masks
+    (1, 48, 128, 2000, 2048, 64, 64, 0.5, True),     # 12 waves, 6 blocks per group; last group partial
+    (1, 48, 64, 2000, 1900, 128, 128, 0.6, False),   # 12 waves, 3 blocks per group; shared mask
+    (2, 20, 128, 2048, 2048, 128, 64, 0.4, True),    # 8 waves, 2 blocks per group
+]
+
+
+@pytest.mark.parametrize("case", GROUPED_CASES, ids=[str(i) for i in range(len(GROUPED_CASES))])
+def test_grouped_query_blocks(case):
+    """Grouped runs (union of a group's kept blocks) equal ungrouped runs (bit for bit where
+    both walk whole tiles), and sampled rows match the oracle."""
+    B, H, D, nq, nk, bq, bk, dens, per_head = case
+    slabs = B * H if per_head else 1
+    scale = D ** -0.5
+    q, k, v = rand((B, nq, H, D), torch.bfloat16, 70), rand((B, nk, H, D), torch.bfloat16, 71), \
+        rand((B, nk, H, D), torch.bfloat16, 72)
+    nbq, nbk = -(-nq // bq), -(-nk // bk)
+    rng = np.random.default_rng(73)
+    keep = rng.random((slabs * nbq, nbk)) < dens
+    keep[np.arange(slabs * nbq), rng.integers(0, nbk, size=slabs * nbq)] = True
+    keep[1] = False                                           # an empty row
+    rp, ci = oracle.csr_from_bool(keep)
+    rpd, cid = torch.from_numpy(rp).to(DEV), torch.from_numpy(ci).to(DEV)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    assert vsa.attn_fwd_workspace_bytes(qd, kd, rpd, cid, bq, bk, slabs) > 0   # this case does group
+    o_g, l_g = vsa.vsa_block_sparse_attn_fwd(qd, kd, vd, rpd, cid, bq, bk, slabs, scale)
+    o_u, l_u = vsa.vsa_block_sparse_attn_fwd(qd, kd, vd, rpd, cid, bq, bk, slabs, scale, grouped=False)
+    if bq > 64:    # both walk each row's tiles whole and in the same order
+        assert torch.equal(o_g, o_u) and torch.equal(l_g, l_u)
+    else:          # ungrouped 64-row blocks split each tile between two waves: another summation order
+        assert (o_g.float() - o_u.float()).abs().max() <= BF16_MAX
+    errs = []
+    for b, h in ((0, 0), (B - 1, H - 1), (0, H // 2)):
+        rows = np.concatenate([np.arange(bq, 2 * bq), rng.choice(nq, 64, replace=False), [nq - 1]])
+        base = 0 if slabs == 1 else (b * H + h) * nbq
+        ref, _ = oracle.attention_rows(to_np(q[b, rows, h]), rows, to_np(k[b, :, h]), to_np(v[b, :, h]),
+                                       rp, ci, base, bq, bk, scale)
+        errs.append(np.abs(o_g[b, rows, h].cpu().double().numpy() - ref))
+    err = np.concatenate(errs)
+    assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN
