@@ -39,7 +39,7 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 METRIC = "block-sparse attn effective TFLOPS (kept blocks), % bf16 MFMA peak; speedup vs dense"
 ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_masks_amd", "csrc", "attn_fwd.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_sta_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_{}_traffic.json")
 
 DESCRIPTION = {
     "sta": "sta: 1 x 24 heads x 115,200 tokens (30x48x80 grid), head_dim 128, bf16, 6x8x8 tiles "
@@ -73,12 +73,22 @@ def attn_flops(rp, ci, block_q, block_k, nq, nk, D, bh, n_slabs):
     return 4.0 * D * total * (bh if n_slabs == 1 else 1)
 
 
-def attn_kernel_name(D, block_q):
-    """The bf16 instantiation the library launches for this block size (the library picks
-    4-wave key-split, 12-, 8- or 4-wave workgroups from block_q)."""
+def attn_kernel_name(D, block_q, grouped=False, batch=1, heads=1, n_qblocks=1):
+    """Label of the bf16 instantiation the library launches.  Query blocks of <= 128 rows
+    are grouped (when the library asks for a workspace) into 12-, 8- or 4-wave
+    workgroups, the first width whose group count keeps enough workgroups; otherwise it
+    picks a 4-wave key split (<= 64 rows) or 12-, 8- or 4-wave workgroups from block_q."""
+    if grouped:
+        wpb = -(-block_q // 32)
+        for nw in (12, 8, 4):
+            G = nw // wpb
+            if nw % wpb or G < 2:
+                continue
+            if batch * heads * -(-n_qblocks // G) >= (512 if nw == 4 else 256):
+                return f"attn_fwd_bf16_kernel<{D}, 1, {nw}, true>"
     ks = 2 if block_q <= 64 else 1
     nw = 4 if ks == 2 else (12 if block_q % 384 == 0 else (8 if block_q % 256 == 0 else 4))
-    return f"attn_fwd_bf16_kernel<{D}, {ks}, {nw}>"
+    return f"attn_fwd_bf16_kernel<{D}, {ks}, {nw}, false>"
 
 
 def source_hash(path):
@@ -372,8 +382,8 @@ def main():
           f"{100 * sics['ratio_to_attn']:.2f}% of attention", file=sys.stderr, flush=True)
 
     traffic = None
-    if name == "sta" and os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
+    if os.path.exists(TRAFFIC_FILE.format(name)):
+        with open(TRAFFIC_FILE.format(name)) as f:
             tr = json.load(f)
         if tr.get("attn_src_sha256_16") == source_hash(ATTN_SRC):
             traffic = tr.get("bytes_per_launch")
@@ -405,7 +415,7 @@ def main():
                    "parallelism": "none (one GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": attn_kernel_name(path.D, path.bq),
+                     "traffic": traffic, "kernel": attn_kernel_name(path.D, path.bq, path.ws is not None, path.B, path.H, path.nbq),
                      "flops_per_launch": flops, "ms_per_launch": round(attn_ms, 4)},
         "cpu_baseline": cpu,
         "attn_tflops": round(attn_tflops, 2),
