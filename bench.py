@@ -4,6 +4,9 @@ A step is one pass of the whole path over one batch of synthetic input, all on
 the GPU with the inputs resident in HBM:
     [tile reorder of Q, K, V] -> block mask -> block-sparse attention ->
     [inverse reorder of O]
+For the STA workloads (sta, sta_heads) the reorder is folded into the attention
+kernel's row addresses (vsa_tiled_attn_fwd on raster-order tokens): the step is
+the mask, then that call; --unfused runs the separate passes instead.
 The default workload is the STA one (24 heads, head_dim 128, bf16, 30x48x80 =
 115,200 tokens, 6x8x8 tiles = 384-token blocks on a 5x6x10 tile grid, 3x3x5 tile
 window clipped at the border); --workload nabla | radial | ar | nabla_sta |
@@ -20,7 +23,7 @@ cpu_baseline= the fp64 oracle on a bounded sample (the same path for a subset of
               heads), FLOPs counted the same way (STA workload only).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sta]
-                       [--no-dense] [--no-cpu]
+                       [--no-dense] [--no-cpu] [--no-bwd] [--unfused]
 """
 import argparse
 import hashlib
@@ -73,11 +76,12 @@ def attn_flops(rp, ci, block_q, block_k, nq, nk, D, bh, n_slabs):
     return 4.0 * D * total * (bh if n_slabs == 1 else 1)
 
 
-def attn_kernel_name(D, block_q, grouped=False, batch=1, heads=1, n_qblocks=1):
+def attn_kernel_name(D, block_q, grouped=False, batch=1, heads=1, n_qblocks=1, tiled=False):
     """Label of the bf16 instantiation the library launches.  Query blocks of <= 128 rows
     are grouped (when the library asks for a workspace) into 12-, 8- or 4-wave
     workgroups, the first width whose group count keeps enough workgroups; otherwise it
-    picks a 4-wave key split (<= 64 rows) or 12-, 8- or 4-wave workgroups from block_q."""
+    picks a 4-wave key split (<= 64 rows) or 12-, 8- or 4-wave workgroups from block_q.  The last
+    flag: raster-order tokens with the tiles as blocks (the fused tile reorder)."""
     if grouped:
         wpb = -(-block_q // 32)
         for nw in (12, 8, 4):
@@ -85,10 +89,10 @@ def attn_kernel_name(D, block_q, grouped=False, batch=1, heads=1, n_qblocks=1):
             if nw % wpb or G < 2:
                 continue
             if batch * heads * -(-n_qblocks // G) >= (512 if nw == 4 else 256):
-                return f"attn_fwd_bf16_kernel<{D}, 1, {nw}, true>"
+                return f"attn_fwd_bf16_kernel<{D}, 1, {nw}, true, {str(tiled).lower()}>"
     ks = 2 if block_q <= 64 else 1
     nw = 4 if ks == 2 else (12 if block_q % 384 == 0 else (8 if block_q % 256 == 0 else 4))
-    return f"attn_fwd_bf16_kernel<{D}, {ks}, {nw}, false>"
+    return f"attn_fwd_bf16_kernel<{D}, {ks}, {nw}, false, {str(tiled).lower()}>"
 
 
 def source_hash(path):
@@ -129,9 +133,12 @@ def cpu_baseline(x, cfg, target_s=12.0):
 class Path:
     """Device buffers and the calls of one workload's path (no allocation per step)."""
 
-    def __init__(self, name, cfg, x, dev):
+    def __init__(self, name, cfg, x, dev, unfused=False):
         import block_sparse_attention_masks_amd as vsa
         self.vsa, self.name, self.dev = vsa, name, dev
+        # STA masks read no token data, so the step runs on raster-order tokens with the
+        # tile reorder folded into the attention kernel (vsa_tiled_attn_fwd)
+        self.fused = name in ("sta", "sta_heads") and not unfused
         B, H, D = cfg["batch"], cfg["heads"], cfg["head_dim"]
         self.B, self.H, self.D = B, H, D
         self.q, self.k, self.v = (x[w].to(dev) for w in ("q", "k", "v"))
@@ -201,6 +208,8 @@ class Path:
         # workspace of the forward (union lists when small query blocks run grouped), sized
         # once: the step allocates nothing
         nws = vsa.attn_fwd_workspace_bytes(self.qa, self.ka, self.rp, self.ci, self.bq, self.bk, self.n_slabs)
+        if self.fused:
+            nws = max(nws, vsa.tiled_attn_workspace_bytes(self.q, *self.tiled, self.rp, self.ci, self.n_slabs))
         self.ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
         self.compact = None
         if name == "ar_compact":
@@ -221,6 +230,8 @@ class Path:
             self.compact = compact
 
     def stages(self):
+        if self.fused:
+            return [("mask", self.mask), ("attn", self.attn)]
         out = [("reorder_in", self.reorder_in), ("mask", self.mask)]
         if self.compact is not None:
             out.append(("compact", self.compact))
@@ -232,6 +243,17 @@ class Path:
                 self.vsa.vsa_tile_reorder(src, *self.tiled, out=dst)
 
     def attn(self, rp=None, ci=None, ws=None):
+        if self.fused:   # raster q, k, v -> raster o and lse
+            wsx = self.ws if rp is None else ws
+            self.vsa.vsa_tiled_attn_fwd(self.q, self.k, self.v, *self.tiled, self.rp if rp is None else rp,
+                                        self.ci if ci is None else ci, self.n_slabs if rp is None else 1,
+                                        self.scale, out=self.o, lse=self.lse, workspace=wsx,
+                                        grouped=wsx is not None)
+            return
+        self.attn_tile_order(rp, ci, ws)
+
+    def attn_tile_order(self, rp=None, ci=None, ws=None):
+        """The forward on the attention-order (tile-major) tensors qa, ka, va -> oa, lse."""
         if rp is None and self.compact is not None:   # over the compact cache
             self.vsa.vsa_block_sparse_attn_fwd(self.qa, self.kc, self.vc, self.rp, self.cc, self.bq, self.bk,
                                                self.n_slabs, self.scale, out=self.oa, lse=self.lse,
@@ -258,6 +280,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="sta / sta_heads: run the tile reorder as its own passes around the attention")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the path shards by head "
@@ -274,7 +298,7 @@ def main():
     t_gen = time.perf_counter()
     x = gen.make_inputs(name)
     print(f"[bench] {name}: inputs generated in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
-    path = Path(name, cfg, x, dev)
+    path = Path(name, cfg, x, dev, unfused=args.unfused)
     stream = torch.cuda.current_stream(dev)
     stage_fns = path.stages()
     stages = tuple(n_ for n_, _ in stage_fns)
@@ -315,7 +339,8 @@ def main():
     dense = None
     if not args.no_dense:
         drp, dci = path.vsa.all_ones_mask(path.nbq, path.nbk, dev)
-        nwd = path.vsa.attn_fwd_workspace_bytes(path.qa, path.ka, drp, dci, path.bq, path.bk, 1)
+        nwd = (path.vsa.tiled_attn_workspace_bytes(path.q, *path.tiled, drp, dci, 1) if path.fused else
+               path.vsa.attn_fwd_workspace_bytes(path.qa, path.ka, drp, dci, path.bq, path.bk, 1))
         dws = torch.empty(nwd, dtype=torch.uint8, device=dev) if nwd else None
         path.attn(drp, dci, dws)
         dms = []
@@ -334,12 +359,14 @@ def main():
     # Backward over the same mask (gradients of sum(dO * O)), timed on its own after the
     # forward, with a seeded dO.  FLOPs are counted as 2.5x the forward's kept-block FLOPs
     # (the five products S, dP, dV, dQ, dK); recomputing S and dP in both kernels is not counted.
+    if path.fused:   # the backward and SICS legs take the attention-order (tile-major) tensors
+        path.reorder_in()
     bwd = None
     if not args.no_bwd:
         kx, vx, cx = ((path.kc, path.vc, path.cc) if path.compact is not None else (path.ka, path.va, path.ci))
         gd = torch.Generator(device=dev).manual_seed(7)
         dout = torch.randn(path.oa.shape, generator=gd, device=dev).to(path.oa.dtype)
-        path.attn()
+        path.attn_tile_order()
         dq_, dk_, dv_ = (torch.empty(t.shape, dtype=torch.float32, device=dev) for t in (path.qa, kx, vx))
         bargs = (path.qa, kx, vx, path.oa, dout, path.lse, path.rp, cx, path.bq, path.bk, path.n_slabs, path.scale)
         wsb = torch.empty(max(1, path.vsa.attn_bwd_workspace_bytes(*bargs)), dtype=torch.uint8, device=dev)
@@ -394,7 +421,7 @@ def main():
         print(f"[bench] cpu baseline {cpu['value']:.4f} TFLOP/s ({cpu['sample']})", file=sys.stderr, flush=True)
 
     token_bytes = path.q.numel() * path.q.element_size()
-    reorder_ms = float(np.mean(ev["reorder_in"]) + np.mean(ev["reorder_out"]))
+    reorder_ms = (float(np.mean(ev["reorder_in"]) + np.mean(ev["reorder_out"])) if "reorder_in" in ev else None)
     out = {
         "metric": METRIC,
         "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
@@ -415,7 +442,8 @@ def main():
                    "parallelism": "none (one GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": attn_kernel_name(path.D, path.bq, path.ws is not None, path.B, path.H, path.nbq),
+                     "traffic": traffic, "kernel": attn_kernel_name(path.D, path.bq, path.ws is not None, path.B, path.H, path.nbq,
+                                                                 path.fused),
                      "flops_per_launch": flops, "ms_per_launch": round(attn_ms, 4)},
         "cpu_baseline": cpu,
         "attn_tflops": round(attn_tflops, 2),
@@ -432,7 +460,11 @@ def main():
                            "ms": round(float(np.mean(ev["compact"])), 4),
                            "bytes_moved": 2 * 2 * path.B * path.n_out * path.H * path.D * path.k.element_size()}),
         "mask_over_attn": round(float(np.mean(ev["mask"])) / attn_ms, 5),
-        "reorder_gbs": (round(4 * 2 * token_bytes / (reorder_ms * 1e-3) / 1e9, 1) if path.tiled else None),
+        "reorder_gbs": (round(4 * 2 * token_bytes / (reorder_ms * 1e-3) / 1e9, 1)
+                        if path.tiled and reorder_ms else None),
+        "tile_reorder": (None if not path.tiled else
+                         "folded into the attention kernel (raster-order q, k, v, o)" if path.fused else
+                         "separate passes: q, k, v in, o out"),
     }
     print(json.dumps(out), flush=True)
 

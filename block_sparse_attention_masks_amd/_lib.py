@@ -47,6 +47,8 @@ _SIGS = {
                         ctypes.POINTER(Select), _P, _P, _I64, _P, ctypes.POINTER(ctypes.c_size_t), _P], _I32),
     "vsa_block_sparse_attn_fwd": ([_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I64, _I64, _I32, _I32,
                                    _P, _P, _I32, _F32, _P, ctypes.POINTER(ctypes.c_size_t), _P], _I32),
+    "vsa_tiled_attn_fwd": ([_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                            _P, _P, _I32, _F32, _P, ctypes.POINTER(ctypes.c_size_t), _P], _I32),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -390,7 +392,8 @@ def vsa_block_sparse_attn_fwd(q, k, v, row_ptr, col_idx, block_q, block_k, n_sla
 
     Small query blocks run grouped (several blocks per workgroup over the union of their
     kept blocks) when a workspace is available: it is allocated here unless given, and
-    grouped=False runs without one (same results, bit for bit)."""
+    grouped=False runs without one (same results; bit for bit for blocks of 65 to 128 rows,
+    to rounding for blocks of at most 64 rows, whose ungrouped run splits each key tile)."""
     for name, t in (("q", q), ("k", k), ("v", v), ("row_ptr", row_ptr), ("col_idx", col_idx)):
         _require(t, name, q.device)
     B, nq, Hh, D = q.shape
@@ -424,6 +427,58 @@ def vsa_block_sparse_attn_fwd(q, k, v, row_ptr, col_idx, block_q, block_k, n_sla
                                            ctypes.byref(nb) if workspace is not None else None, _stream(q)),
            "vsa_block_sparse_attn_fwd")
     return out, lse
+
+
+def vsa_tiled_attn_fwd(q, k, v, grid, tile, row_ptr, col_idx, n_slabs=1, scale=None, out=None, lse=None,
+                       want_lse=True, workspace=None, grouped=True):
+    """Attention on raster-order tokens of a T x H x W grid whose tt x th x tw tiles (in
+    tile-major order) are the blocks -> (o, lse or None), both in raster order.  Equals
+    tile reorder -> vsa_block_sparse_attn_fwd -> inverse reorder, with the permutation
+    applied to the row addresses inside the kernel instead of to the tensors."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("row_ptr", row_ptr), ("col_idx", col_idx)):
+        _require(t, name, q.device)
+    (T, H, W), (tt, th, tw) = grid, tile
+    B, n, Hh, D = q.shape
+    if n != T * H * W or k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must all be [batch, T*H*W, heads, head_dim] of one dtype")
+    if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise ValueError("row_ptr and col_idx must be int32")
+    n_tiles = (T // tt) * (H // th) * (W // tw)
+    if row_ptr.numel() != n_slabs * n_tiles + 1:
+        raise ValueError("row_ptr length does not match n_slabs * n_tiles + 1")
+    scale = D ** -0.5 if scale is None else scale
+    out = torch.empty_like(q) if out is None else out
+    _require(out, "out", q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hh, n), dtype=torch.float32, device=q.device)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _DTYPE[q.dtype], B, Hh, D, T, H, W, tt, th, tw,
+            _ptr(row_ptr), _ptr(col_idx), n_slabs, float(scale))
+    nb = ctypes.c_size_t(0)
+    if grouped:
+        if workspace is None:
+            _check(lib().vsa_tiled_attn_fwd(*args, None, ctypes.byref(nb), _stream(q)), "vsa_tiled_attn_fwd")
+            if nb.value:
+                workspace = torch.empty(nb.value, dtype=torch.uint8, device=q.device)
+        if workspace is not None:
+            _require(workspace, "workspace", q.device)
+            nb = ctypes.c_size_t(workspace.numel())
+    else:
+        workspace = None
+    _check(lib().vsa_tiled_attn_fwd(*args, _ptr(workspace) if workspace is not None else None,
+                                    ctypes.byref(nb) if workspace is not None else None, _stream(q)),
+           "vsa_tiled_attn_fwd")
+    return out, lse
+
+
+def tiled_attn_workspace_bytes(q, grid, tile, row_ptr, col_idx, n_slabs=1):
+    """Workspace bytes vsa_tiled_attn_fwd uses to group small tiles (0: none)."""
+    (T, H, W), (tt, th, tw) = grid, tile
+    B, n, Hh, D = q.shape
+    nb = ctypes.c_size_t(0)
+    _check(lib().vsa_tiled_attn_fwd(_ptr(q), _ptr(q), _ptr(q), _ptr(q), None, _DTYPE[q.dtype], B, Hh, D, T, H, W,
+                                    tt, th, tw, _ptr(row_ptr), _ptr(col_idx), n_slabs, D ** -0.5, None,
+                                    ctypes.byref(nb), _stream(q)), "vsa_tiled_attn_fwd")
+    return nb.value
 
 
 def attn_fwd_workspace_bytes(q, k, row_ptr, col_idx, block_q, block_k, n_slabs=1):

@@ -25,7 +25,7 @@ vsa_status check_tokens(int32_t dtype, int64_t batch, int32_t heads, int32_t hea
       block_k <= 0)
     return VSA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return VSA_ERR_UNSUPPORTED;
-  if (nq > kI32Max || nk > kI32Max) return VSA_ERR_SHAPE;
+  if (nq > kI32Max - 64 || nk > kI32Max - 64) return VSA_ERR_SHAPE;  // 64-key tiles step in 31 bits
   if (batch * heads * ceil_div(nq, block_q) > kI32Max) return VSA_ERR_SHAPE;
   return VSA_OK;
 }
@@ -239,6 +239,41 @@ vsa_status vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v
   if (!(scale > 0.0f) || scale == INFINITY) return VSA_ERR_PARAM;
   vsa::AttnArgs a{q, k, v, o, lse, dtype, batch, heads, head_dim, nq, nk, block_q, block_k,
                   row_ptr, col_idx, n_slabs, scale};
+  const size_t want = dtype == VSA_BF16 ? vsa::attn_fwd_workspace(a) : 0;
+  if (workspace_bytes && !workspace) {  // size query
+    *workspace_bytes = want;
+    return VSA_OK;
+  }
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return VSA_ERR_UNSUPPORTED;
+  if (workspace && ((uintptr_t)workspace & 255u)) return VSA_ERR_UNSUPPORTED;
+  const size_t have = workspace && workspace_bytes ? *workspace_bytes : 0;
+  return from_hip(vsa::launch_attn_fwd(a, workspace, have, stream));
+}
+
+vsa_status vsa_tiled_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int32_t dtype, int64_t batch, int32_t heads, int32_t head_dim,
+                              int32_t T, int32_t H, int32_t W, int32_t tt, int32_t th, int32_t tw,
+                              const int32_t* row_ptr, const int32_t* col_idx, int32_t n_slabs,
+                              float scale, void* workspace, size_t* workspace_bytes,
+                              hipStream_t stream) {
+  if (!q || !k || !v || !o || !row_ptr || !col_idx) return VSA_ERR_NULL;
+  if (T <= 0 || H <= 0 || W <= 0 || tt <= 0 || th <= 0 || tw <= 0) return VSA_ERR_SHAPE;
+  if (T % tt || H % th || W % tw) return VSA_ERR_SHAPE;
+  const int64_t n = (int64_t)T * H * W, block = (int64_t)tt * th * tw;
+  if (n > kI32Max || block > kI32Max) return VSA_ERR_SHAPE;
+  vsa_status st = check_tokens(dtype, batch, heads, head_dim, n, n, (int32_t)block, (int32_t)block);
+  if (st != VSA_OK) return st;
+  if (n_slabs != 1 && (int64_t)n_slabs != batch * heads) return VSA_ERR_PARAM;
+  if (!(scale > 0.0f) || scale == INFINITY) return VSA_ERR_PARAM;
+  if (vsa::tiling_mode(th, tw) == 0) return VSA_ERR_UNSUPPORTED;
+  vsa::AttnArgs a{q, k, v, o, lse, dtype, batch, heads, head_dim, n, n, (int)block, (int)block,
+                  row_ptr, col_idx, n_slabs, scale};
+  a.tiled = 1;
+  a.H = H;
+  a.W = W;
+  a.tt = tt;
+  a.th = th;
+  a.tw = tw;
   const size_t want = dtype == VSA_BF16 ? vsa::attn_fwd_workspace(a) : 0;
   if (workspace_bytes && !workspace) {  // size query
     *workspace_bytes = want;

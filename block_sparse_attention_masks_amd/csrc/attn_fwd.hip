@@ -33,6 +33,8 @@
 // one thread per query row (used for small fp32 problems).
 #include <math.h>
 
+#include <type_traits>
+
 #include "vsa_internal.h"
 
 namespace vsa {
@@ -63,19 +65,78 @@ struct Groups {
   int G, wpb, cap;
 };
 
+// Tokens in raster order of a T x H x W grid cut into tt x th x tw tiles, the attention
+// blocks being the tiles in tile-major order (the order the tile reorder produces: STA,
+// "Sliding tile attention", sec. 3): the rows are mapped on the fly instead of moved.
+// NH, NW: tiles along H and W; P = th tw; V = tt P (tokens per tile); HW = H W.  A 64-row
+// copy tile at within-tile offset r0 (a multiple of 64) sits at raster rows
+// tile start + uni(r0) + lane(r) when the tile's h-w plane and the copy tile nest:
+//   mode 1: P % 64 == 0 and tw | 64;  mode 2: P % 64 == 0 and 64 | tw;  mode 3: P | 64.
+struct Tiling {
+  int H, W, tt, th, tw, NH, NW, P, V, HW, mode;
+  int dw, dh, dt;  // copy-tile advance in (w, h, t) within a tile: (0, 64 / tw, 0), (64, 0, 0)
+                   // or (0, 0, 64 / P) in modes 1, 2, 3
+  // n / d = (n m) >> (31 + l) for n < 2^31, with l = ceil(log2 d) and m = ceil(2^(31 + l) / d)
+  // (the round-up reciprocal of Granlund and Montgomery): for d = NH NW and d = NW
+  uint32_t m_plane, m_nw;
+  int l_plane, l_nw;
+};
+
+__device__ inline uint32_t div_magic(uint32_t n, uint32_t m, int l) {
+  return (uint32_t)(((uint64_t)n * m) >> (31 + l));
+}
+// Raster row of the first token of tile `tile` (tile-major tile index).
+__device__ inline int tile_start(const Tiling& t, int tile) {
+  const uint32_t it_ = div_magic((uint32_t)tile, t.m_plane, t.l_plane);
+  const uint32_t rem = (uint32_t)tile - it_ * (uint32_t)(t.NH * t.NW);
+  const uint32_t ih = div_magic(rem, t.m_nw, t.l_nw), iw = rem - ih * (uint32_t)t.NW;
+  return (int)(it_ * t.tt * t.HW + ih * t.th * t.W + iw * t.tw);
+}
+
+// Raster row (within one batch entry) of tile-major position p; every value is below
+// the T H W tokens, which fit 31 bits.
+__device__ inline int raster_row(const Tiling& t, int p) {
+  const unsigned up = (unsigned)p, V = (unsigned)t.V, P = (unsigned)t.P, tw = (unsigned)t.tw;
+  const unsigned tile = up / V, r = up - tile * V;
+  const unsigned plane = (unsigned)(t.NH * t.NW), it_ = tile / plane, rem = tile - it_ * plane;
+  const unsigned ih = rem / (unsigned)t.NW, iw = rem - ih * (unsigned)t.NW;
+  const unsigned lt = r / P, rr = r - lt * P, lh = rr / tw, lw = rr - lh * tw;
+  return (int)((it_ * t.tt + lt) * t.HW + (ih * t.th + lh) * t.W + iw * tw + lw);
+}
+// lane part for row r (0..63) of a full copy tile
+__device__ inline int tile_lane(const Tiling& t, int r) {
+  if (t.mode == 1) return (r / t.tw) * t.W + r % t.tw;
+  if (t.mode == 2) return r;
+  const int lt = r / t.P, rr = r - lt * t.P;
+  return lt * t.HW + (rr / t.tw) * t.W + rr % t.tw;
+}
+
 // Stream of 64-key tiles over the kept blocks of one CSR row (wave-uniform).
+// Key indices fit 31 bits with 64 to spare (the call checks nk), so the stream is walked
+// in 32-bit scalar arithmetic.
 struct TileIter {
   const int32_t* col;
   int e, e1;
-  int64_t k0, ke;
+  int k0, ke;
   int block_k;
-  int64_t nk;
+  int nk;
+  int ks = 0;  // first key of the current block
+  // tiled: raster row of the block's first token, and the current copy tile's first row
+  // within the tile, (lt, lh, lw), with its raster offset uo = lt HW + lh W + lw
+  int rb = 0, lt = 0, lh = 0, lw = 0, uo = 0;
   __device__ bool valid() const { return e < e1; }
   __device__ void open() {  // position on the first tile of block col[e]
     if (e < e1) {
-      const int64_t ks = (int64_t)col[e] * block_k;
+      ks = col[e] * block_k;
       k0 = ks;
-      ke = min(ks + block_k, nk);
+      ke = block_k < nk - ks ? ks + block_k : nk;
+    }
+  }
+  __device__ void open(const Tiling& t) {
+    open();
+    if (e < e1) {
+      rb = tile_start(t, col[e]);  // a block is a tile
+      lt = lh = lw = uo = 0;
     }
   }
   __device__ void next() {
@@ -84,6 +145,24 @@ struct TileIter {
       ++e;
       open();
     }
+  }
+  __device__ void next(const Tiling& t) {
+    k0 += kBN;
+    if (k0 >= ke) {
+      ++e;
+      open(t);
+      return;
+    }
+    // the next 64 rows of the same tile (only full copy tiles are followed by another):
+    // advance w, carry into h, carry into t; selects, no branches
+    lw += t.dw;
+    const int cw = lw >= t.tw;
+    lw -= cw * t.tw;
+    lh += t.dh + cw;
+    const int ch = lh >= t.th;
+    lh -= ch * t.th;
+    lt += t.dt + ch;
+    uo = lt * t.HW + lh * t.W + lw;
   }
 };
 
@@ -183,13 +262,13 @@ struct Smem {
   uint16_t v[2][kBN * D];
 };
 
-template <int D, int KS, int NW, bool GR>
+template <int D, int KS, int NW, bool GR, bool TL>
 __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
     int64_t nq, int64_t nk, int heads, int block_q, int block_k,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int n_slabs,
-    float scale_log2, Work wk, Groups gp) {
+    float scale_log2, Work wk, Groups gp, Tiling tg) {
   __shared__ __attribute__((aligned(1024))) Smem<D> sm;
   static_assert(KS == 1 || NW == 4, "key split runs with 4 waves");
   static_assert(!GR || KS == 1, "grouped query blocks use whole tiles");
@@ -237,12 +316,13 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
   TileIter it;
   if constexpr (GR) {  // the union of the group's kept blocks, with a row-membership mask
     const int64_t u = slab * wk.nbq + qb;
-    it = TileIter{gp.col, (int)(u * gp.cap), (int)(u * gp.cap) + gp.cnt[u], 0, 0, block_k, nk};
+    it = TileIter{gp.col, (int)(u * gp.cap), (int)(u * gp.cap) + gp.cnt[u], 0, 0, block_k, (int)nk};
   } else {
     const int64_t r = slab * wk.nbq + qb;
-    it = TileIter{col_idx, row_ptr[r], row_ptr[r + 1], 0, 0, block_k, nk};
+    it = TileIter{col_idx, row_ptr[r], row_ptr[r + 1], 0, 0, block_k, (int)nk};
   }
-  it.open();
+  if constexpr (TL) it.open(tg);
+  else it.open();
   const uint16_t* kbase = k + (b * nk * heads + h) * (int64_t)D;
   const uint16_t* vbase = v + (b * nk * heads + h) * (int64_t)D;
 
@@ -259,35 +339,66 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
     lrow[j] = cb * RPC + l / SPR;
     ch16[j] = 16u * ((l % SPR) ^ (c < CB ? swz_k<D>(lrow[j]) : swz_v<D>(lrow[j])));
   }
-  auto issue = [&](int64_t k0, int64_t ke, int stage) {
-    const char* kt = (const char*)(kbase + k0 * row_stride);
-    const char* vt = (const char*)(vbase + k0 * row_stride);
-    const int last = (int)min(ke - k0, (int64_t)kBN) - 1;
+  int loff[NJ];  // tiled: lane part of row lrow[j] of a full copy tile
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int c = w + NW * j;
-      if (c < 2 * CB) {
-        const uint32_t ro = __umul24((uint32_t)min(lrow[j], last), row_bytes) + ch16[j];
-        if (c < CB)
-          load_lds16((const uint16_t*)(kt + ro), sm.k[stage] + c * 512);
-        else
-          load_lds16((const uint16_t*)(vt + ro), sm.v[stage] + (c - CB) * 512);
+  for (int j = 0; j < NJ; ++j) loff[j] = TL ? tile_lane(tg, lrow[j]) : 0;
+  auto issue = [&](const TileIter& t_, int stage) {
+    const int k0 = t_.k0, ke = t_.ke;
+    const int last = min(ke - k0, kBN) - 1;
+    if constexpr (TL) {
+      // rows of a full copy tile: tile start + uniform part + lane part; a partial one
+      // (a tile shorter than 64 tokens) maps row by row, on a branch of its own
+      int rows[NJ];
+      if (last == kBN - 1) {
+        const int base_row = t_.rb + t_.uo;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) rows[j] = base_row + loff[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) rows[j] = raster_row(tg, k0 + min(lrow[j], last));
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int c = w + NW * j;
+        if (c < 2 * CB) {
+          const uint64_t ro = (uint64_t)(uint32_t)rows[j] * row_bytes + ch16[j];
+          if (c < CB)
+            load_lds16((const uint16_t*)((const char*)kbase + ro), sm.k[stage] + c * 512);
+          else
+            load_lds16((const uint16_t*)((const char*)vbase + ro), sm.v[stage] + (c - CB) * 512);
+        }
+      }
+    } else {
+      const char* kt = (const char*)(kbase + (int64_t)k0 * row_stride);
+      const char* vt = (const char*)(vbase + (int64_t)k0 * row_stride);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int c = w + NW * j;
+        if (c < 2 * CB) {
+          const uint32_t ro = __umul24((uint32_t)min(lrow[j], last), row_bytes) + ch16[j];
+          if (c < CB)
+            load_lds16((const uint16_t*)(kt + ro), sm.k[stage] + c * 512);
+          else
+            load_lds16((const uint16_t*)(vt + ro), sm.v[stage] + (c - CB) * 512);
+        }
       }
     }
   };
 
   const int64_t my_q = q_w + col;
+  // row of this lane's query in q, o and lse (tiled: its raster row)
+  const int64_t my_row = TL && my_q < q_hi ? (int64_t)raster_row(tg, (int)my_q) : my_q;
   bf16x8 qf[D / 16];
   {
     const bool ok = my_q < q_hi;
-    const uint16_t* qp = q + ((b * nq + (ok ? my_q : 0)) * heads + h) * D + 8 * g;
+    const uint16_t* qp = q + ((b * nq + (ok ? my_row : 0)) * heads + h) * D + 8 * g;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       u32x4 u = ok ? *(const u32x4*)(qp + 16 * s) : u32x4{0, 0, 0, 0};
       qf[s] = __builtin_bit_cast(bf16x8, u);
     }
   }
-  if (it.valid()) issue(it.k0, it.ke, 0);
+  if (it.valid()) issue(it, 0);
 
   f32x16 acc_o[D / 32];
 #pragma unroll
@@ -305,12 +416,19 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
   wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
 
+  // nx (the tile after it) is advanced one iteration ahead, after the products are issued,
+  // so the scalar work of the walk is not queued on the scalar unit by every wave at once
+  // at the top of the loop, where it would delay the copies and the first products
+  auto advance = [&](TileIter& t_) {
+    if constexpr (TL) t_.next(tg);
+    else t_.next();
+  };
+  TileIter nx = it;
+  advance(nx);
   int buf = 0;
   while (it.valid()) {
-    const int valid = (int)min((int64_t)kBN, it.ke - it.k0);
-    TileIter nx = it;
-    nx.next();
-    if (nx.valid()) issue(nx.k0, nx.ke, buf ^ 1);
+    const int valid = min(kBN, it.ke - it.k0);
+    if (nx.valid()) issue(nx, buf ^ 1);
     const uint16_t* sk = sm.k[buf];
     const uint16_t* sv = sm.v[buf];
     // grouped: a wave whose query block does not keep this key block only helps copy it
@@ -387,10 +505,13 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
         acc_o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t], pf[kk], acc_o[t], 0, 0, 0);
     }
     }
+    TileIter nn = nx;
+    advance(nn);
     wait_vmcnt<0>();               // the next tile's loads have landed
     __builtin_amdgcn_s_barrier();  // ... for everyone; this tile is no longer read
     buf ^= 1;
     it = nx;
+    nx = nn;
   }
 
   // ---- epilogue
@@ -420,7 +541,7 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
   const float l_tot = l_run + xchg32(l_run, g);
   if (my_q < q_hi) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* op = o + ((b * nq + my_q) * heads + h) * D;
+    uint16_t* op = o + ((b * nq + my_row) * heads + h) * D;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
@@ -432,18 +553,18 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
         *(bf16x4*)(op + d) = ov;
       }
     if (lse != nullptr && g == 0)
-      lse[(b * heads + h) * nq + my_q] =
+      lse[(b * heads + h) * nq + my_row] =
           l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f : -INFINITY;
   }
 }
 
 // fp32: one thread per (batch, head, query); plain online softmax over the kept keys.
-template <int D>
+template <int D, bool TL>
 __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, float* __restrict__ lse, int64_t batch, int64_t nq, int64_t nk,
     int heads, int block_q, int block_k, const int32_t* __restrict__ row_ptr,
-    const int32_t* __restrict__ col_idx, int n_slabs, int nbq, float scale) {
+    const int32_t* __restrict__ col_idx, int n_slabs, int nbq, float scale, Tiling tg) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= batch * heads * nq) return;
   const int64_t tq = gid % nq;
@@ -451,7 +572,8 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
   const int64_t b = gid / (nq * heads);
   const int64_t stride = (int64_t)heads * D;
   float qv[D], acc[D];
-  const float* qp = q + (b * nq + tq) * stride + (int64_t)h * D;
+  const int64_t qrow = TL ? (int64_t)raster_row(tg, (int)tq) : tq;  // row in q, o and lse
+  const float* qp = q + (b * nq + qrow) * stride + (int64_t)h * D;
 #pragma unroll
   for (int d = 0; d < D; ++d) {
     qv[d] = qp[d];
@@ -463,8 +585,9 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
   for (int e = row_ptr[r]; e < row_ptr[r + 1]; ++e) {
     const int64_t ks = (int64_t)col_idx[e] * block_k, ke = min(ks + block_k, nk);
     for (int64_t kt = ks; kt < ke; ++kt) {
-      const float* kp = k + (b * nk + kt) * stride + (int64_t)h * D;
-      const float* vp = v + (b * nk + kt) * stride + (int64_t)h * D;
+      const int64_t krow = TL ? (int64_t)raster_row(tg, (int)kt) : kt;
+      const float* kp = k + (b * nk + krow) * stride + (int64_t)h * D;
+      const float* vp = v + (b * nk + krow) * stride + (int64_t)h * D;
       float sdot = 0.f;
 #pragma unroll
       for (int d = 0; d < D; ++d) sdot = fmaf(qv[d], kp[d], sdot);
@@ -477,11 +600,11 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
       m = mn;
     }
   }
-  float* op = o + (b * nq + tq) * stride + (int64_t)h * D;
+  float* op = o + (b * nq + qrow) * stride + (int64_t)h * D;
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
   for (int d = 0; d < D; ++d) op[d] = acc[d] * inv;
-  if (lse != nullptr) lse[(b * heads + h) * nq + tq] = lsum > 0.f ? m + logf(lsum) : -INFINITY;
+  if (lse != nullptr) lse[(b * heads + h) * nq + qrow] = lsum > 0.f ? m + logf(lsum) : -INFINITY;
 }
 
 }  // namespace
@@ -559,25 +682,64 @@ FwdPlan plan_fwd(const AttnArgs& a, bool have_ws) {
   return p;
 }
 
+// Kernel view of the tile grid (a.tiled) and its copy mode; all zero when not tiled.
+Tiling make_tiling(const AttnArgs& a) {
+  Tiling t{};
+  if (!a.tiled) return t;
+  t.H = a.H;
+  t.W = a.W;
+  t.tt = a.tt;
+  t.th = a.th;
+  t.tw = a.tw;
+  t.NH = a.H / a.th;
+  t.NW = a.W / a.tw;
+  t.P = a.th * a.tw;
+  t.V = a.tt * t.P;
+  t.HW = a.H * a.W;
+  t.mode = tiling_mode(a.th, a.tw);
+  t.dw = t.mode == 2 ? kBN : 0;
+  t.dh = t.mode == 1 ? kBN / a.tw : 0;
+  t.dt = t.mode == 3 ? kBN / t.P : 0;
+  auto magic = [](uint32_t d, uint32_t& m, int& l) {
+    l = 0;
+    while ((1ull << l) < d) ++l;
+    m = (uint32_t)(((1ull << (31 + l)) + d - 1) / d);
+  };
+  magic((uint32_t)(t.NH * t.NW), t.m_plane, t.l_plane);
+  magic((uint32_t)t.NW, t.m_nw, t.l_nw);
+  return t;
+}
+
 }  // namespace
+
+int tiling_mode(int th, int tw) {
+  const int P = th * tw;
+  if (P % kBN == 0 && kBN % tw == 0) return 1;
+  if (P % kBN == 0 && tw % kBN == 0) return 2;
+  if (kBN % P == 0) return 3;
+  return 0;
+}
 
 size_t attn_fwd_workspace(const AttnArgs& a) { return plan_fwd(a, true).ws_bytes; }
 
 hipError_t launch_attn_fwd(const AttnArgs& a, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const int nbq = (int)((a.nq + a.block_q - 1) / a.block_q);
+  const Tiling tg = make_tiling(a);
   if (a.dtype == 0) {
     const int64_t n = a.batch * a.heads * a.nq;
     const dim3 grid((unsigned)((n + 255) / 256));
-    if (a.head_dim == 64)
-      hipLaunchKernelGGL(attn_fwd_f32_kernel<64>, grid, dim3(256), 0, stream, (const float*)a.q,
-                         (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.batch, a.nq,
-                         a.nk, a.heads, a.block_q, a.block_k, a.row_ptr, a.col_idx, a.n_slabs, nbq,
-                         a.scale);
-    else
-      hipLaunchKernelGGL(attn_fwd_f32_kernel<128>, grid, dim3(256), 0, stream, (const float*)a.q,
-                         (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.batch, a.nq,
-                         a.nk, a.heads, a.block_q, a.block_k, a.row_ptr, a.col_idx, a.n_slabs, nbq,
-                         a.scale);
+    auto launch32 = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, (const float*)a.q, (const float*)a.k,
+                         (const float*)a.v, (float*)a.o, a.lse, a.batch, a.nq, a.nk, a.heads, a.block_q,
+                         a.block_k, a.row_ptr, a.col_idx, a.n_slabs, nbq, a.scale, tg);
+    };
+    if (a.head_dim == 64) {
+      if (a.tiled) launch32(attn_fwd_f32_kernel<64, true>);
+      else launch32(attn_fwd_f32_kernel<64, false>);
+    } else {
+      if (a.tiled) launch32(attn_fwd_f32_kernel<128, true>);
+      else launch32(attn_fwd_f32_kernel<128, false>);
+    }
     return hipGetLastError();
   }
   const float sl2 = a.scale * kLog2e;
@@ -611,26 +773,31 @@ hipError_t launch_attn_fwd(const AttnArgs& a, void* workspace, size_t workspace_
   auto launch = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(pl.nw * kWave), 0, stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.nq, a.nk,
-                       a.heads, a.block_q, a.block_k, a.row_ptr, a.col_idx, a.n_slabs, sl2, wk, gp);
+                       a.heads, a.block_q, a.block_k, a.row_ptr, a.col_idx, a.n_slabs, sl2, wk, gp, tg);
   };
+  // instantiation for (head_dim, plan, tiled)
+  auto pick = [&](auto dc, auto tc) {
+    constexpr int D = decltype(dc)::value;
+    constexpr bool TL = decltype(tc)::value;
+    if (pl.grouped) {
+      if (pl.nw == 12) launch(attn_fwd_bf16_kernel<D, 1, 12, true, TL>);
+      else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<D, 1, 8, true, TL>);
+      else launch(attn_fwd_bf16_kernel<D, 1, 4, true, TL>);
+    } else if (pl.ks == 2) launch(attn_fwd_bf16_kernel<D, 2, 4, false, TL>);
+    else if (pl.nw == 12) launch(attn_fwd_bf16_kernel<D, 1, 12, false, TL>);
+    else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<D, 1, 8, false, TL>);
+    else launch(attn_fwd_bf16_kernel<D, 1, 4, false, TL>);
+  };
+  using D64 = std::integral_constant<int, 64>;
+  using D128 = std::integral_constant<int, 128>;
+  using Yes = std::integral_constant<bool, true>;
+  using No = std::integral_constant<bool, false>;
   if (a.head_dim == 64) {
-    if (pl.grouped) {
-      if (pl.nw == 12) launch(attn_fwd_bf16_kernel<64, 1, 12, true>);
-      else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<64, 1, 8, true>);
-      else launch(attn_fwd_bf16_kernel<64, 1, 4, true>);
-    } else if (pl.ks == 2) launch(attn_fwd_bf16_kernel<64, 2, 4, false>);
-    else if (pl.nw == 12) launch(attn_fwd_bf16_kernel<64, 1, 12, false>);
-    else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<64, 1, 8, false>);
-    else launch(attn_fwd_bf16_kernel<64, 1, 4, false>);
+    if (a.tiled) pick(D64{}, Yes{});
+    else pick(D64{}, No{});
   } else {
-    if (pl.grouped) {
-      if (pl.nw == 12) launch(attn_fwd_bf16_kernel<128, 1, 12, true>);
-      else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<128, 1, 8, true>);
-      else launch(attn_fwd_bf16_kernel<128, 1, 4, true>);
-    } else if (pl.ks == 2) launch(attn_fwd_bf16_kernel<128, 2, 4, false>);
-    else if (pl.nw == 12) launch(attn_fwd_bf16_kernel<128, 1, 12, false>);
-    else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<128, 1, 8, false>);
-    else launch(attn_fwd_bf16_kernel<128, 1, 4, false>);
+    if (a.tiled) pick(D128{}, Yes{});
+    else pick(D128{}, No{});
   }
   return hipGetLastError();
 }

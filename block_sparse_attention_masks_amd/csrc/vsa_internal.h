@@ -108,7 +108,15 @@ struct AttnArgs {
   const int32_t* col_idx;
   int n_slabs;
   float scale;
+  // tiled: q, k, v, o and lse are in raster order of a T x H x W grid whose tt x th x tw
+  // tiles, in tile-major order, are the attention blocks (block_q = block_k = tt th tw)
+  int tiled = 0;
+  int H = 0, W = 0, tt = 0, th = 0, tw = 0;
 };
+// How a tiled forward maps its 64-row copy tiles (0: the tile shape is not supported):
+// the tile's h-w plane must be a multiple of 64 tokens with tw dividing 64 or a multiple
+// of 64, or divide 64.
+int tiling_mode(int th, int tw);
 // Workspace the bf16 forward uses for grouped query blocks (0 if none); without it the
 // call runs ungrouped.
 size_t attn_fwd_workspace(const AttnArgs& a);

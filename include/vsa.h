@@ -6,7 +6,8 @@
  * CSR list of kept key blocks (vsa_mask_sta, vsa_mask_radial, vsa_mask_nabla; composed
  * with vsa_mask_sta_heads and vsa_mask_union),
  * then compute exact softmax(Q K^T * scale) V over the kept blocks only
- * (vsa_block_sparse_attn_fwd) and its gradients (vsa_block_sparse_attn_bwd).
+ * (vsa_block_sparse_attn_fwd; vsa_tiled_attn_fwd folds the reorder into it) and its
+ * gradients (vsa_block_sparse_attn_bwd).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -291,7 +292,9 @@ vsa_status vsa_mask_nabla(const void* q, const void* k, int32_t dtype,
  * kept key blocks, so one copy of a key tile serves more query rows.  The
  * workspace (device, 256-byte aligned) holds those union lists; with workspace =
  * NULL, or smaller than the query, the call runs ungrouped.  Both give the same
- * result bit for bit.
+ * result bit for bit for query blocks of 65 to 128 rows; ungrouped blocks of at most
+ * 64 rows split each key tile between two waves and add their halves at the end, so
+ * there the two agree to rounding only.
  * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE, VSA_ERR_DTYPE, VSA_ERR_PARAM (n_slabs, scale),
  * VSA_ERR_UNSUPPORTED (head_dim not 64/128, misalignment), VSA_ERR_CAPACITY,
  * VSA_ERR_HIP.  The CSR contents are trusted: column indices must lie in
@@ -305,6 +308,39 @@ vsa_status vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v
                                      int32_t n_slabs, float scale,
                                      void* workspace, size_t* workspace_bytes,
                                      hipStream_t stream);
+
+/*
+ * vsa_tiled_attn_fwd -- the forward above on raster-order tokens of a 3D grid,
+ * with the tiles as blocks and no reorder pass.
+ *
+ * Sliding Tile Attention explainer (aibr.jp/archives/60739), sec. 1-3: sliding
+ * tile attention replaces full 3D attention as a drop-in, Q, K and V in, O out,
+ * same shape; the tile-major order (vsa_tile_reorder) is what makes each tile's
+ * tokens one block.  This call reads q, k, v and writes o and lse in raster order
+ * and applies the tile-major permutation to the row addresses inside the kernel:
+ * the result equals vsa_tile_reorder of q, k, v, then vsa_block_sparse_attn_fwd
+ * with block_q = block_k = tt*th*tw, then the inverse reorder of o (and of lse),
+ * bit for bit, without moving the token tensors through HBM twice.
+ *
+ * q, k, v, o  device, [batch, T*H*W, heads, head_dim] in raster order, dtype,
+ *             16-byte aligned.  lse: NULL or device [batch, heads, T*H*W] fp32, raster
+ *             order.
+ * row_ptr/col_idx  CSR over the tile-major tiles (n_tiles = T/tt * H/th * W/tw rows
+ *             per slab; vsa_mask_sta's output), n_slabs = 1 or batch*heads.
+ * workspace / workspace_bytes, scale: as for vsa_block_sparse_attn_fwd.
+ * The tile's h-w plane must nest with the kernel's 64-token copy tile: th*tw a
+ * multiple of 64 with tw dividing 64 or a multiple of 64, or th*tw dividing 64 (the
+ * 6x8x8 and 1x8x8 tiles of the pages' video models qualify).
+ * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE (non-positive sizes, T/H/W not divisible by
+ * tt/th/tw, T*H*W >= 2^31), VSA_ERR_DTYPE, VSA_ERR_PARAM (n_slabs, scale),
+ * VSA_ERR_UNSUPPORTED (head_dim not 64/128, misalignment, tile shape), VSA_ERR_HIP.
+ */
+vsa_status vsa_tiled_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int32_t dtype, int64_t batch, int32_t heads, int32_t head_dim,
+                              int32_t T, int32_t H, int32_t W, int32_t tt, int32_t th, int32_t tw,
+                              const int32_t* row_ptr, const int32_t* col_idx, int32_t n_slabs,
+                              float scale, void* workspace, size_t* workspace_bytes,
+                              hipStream_t stream);
 
 /*
  * vsa_block_sparse_attn_bwd -- gradients of the forward above.

@@ -140,6 +140,37 @@ def test_attn_validation(L):
     assert attn(L, query=True) == (OK, 0)
 
 
+def tiled(L, q=FAKE, dtype=1, B=1, H=2, D=128, grid=(12, 16, 16), tile=(6, 8, 8), rp=FAKE, ci=FAKE, slabs=1,
+          scale=0.1, query=False):
+    nb = ctypes.c_size_t(123)
+    st = L.vsa_tiled_attn_fwd(q, FAKE, FAKE, FAKE, NULL, dtype, B, H, D, *grid, *tile, rp, ci, slabs, scale,
+                              NULL if query else FAKE, ctypes.byref(nb) if query else None, NULL)
+    return st, nb.value
+
+
+def test_tiled_attn_validation(L):
+    assert tiled(L, q=NULL)[0] == E_NULL
+    assert tiled(L, ci=NULL)[0] == E_NULL
+    assert tiled(L, grid=(12, 16, 15))[0] == E_SHAPE       # W not divisible by tw
+    assert tiled(L, grid=(0, 16, 16))[0] == E_SHAPE
+    assert tiled(L, grid=(2048, 1024, 1024), tile=(1, 8, 8))[0] == E_SHAPE   # 2^31 tokens
+    assert tiled(L, dtype=5)[0] == E_DTYPE
+    assert tiled(L, D=96)[0] == E_UNSUP
+    assert tiled(L, slabs=3)[0] == E_PARAM
+    assert tiled(L, scale=0.0)[0] == E_PARAM
+    assert tiled(L, q=ODD)[0] == E_UNSUP
+    # tile planes that do not nest with the 64-token copy tile
+    assert tiled(L, grid=(9, 9, 9), tile=(3, 3, 3))[0] == E_UNSUP
+    assert tiled(L, grid=(2, 4, 192), tile=(1, 2, 96))[0] == E_UNSUP
+    # supported planes: 64 | th*tw with tw | 64, tw a multiple of 64, th*tw | 64
+    for grid, tile in (((12, 16, 16), (6, 8, 8)), ((2, 24, 32), (1, 12, 16)), ((2, 4, 256), (1, 1, 128)),
+                       ((8, 8, 8), (4, 4, 4)), ((4, 4, 4), (1, 1, 1))):
+        assert tiled(L, grid=grid, tile=tile, query=True)[0] == OK
+    # workspace: none for 384-token tiles, the union lists for 64-token tiles (grouped)
+    assert tiled(L, query=True) == (OK, 0)
+    assert tiled(L, grid=(12, 64, 64), tile=(1, 8, 8), query=True)[1] > 0
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(1, 64, 2, 8)

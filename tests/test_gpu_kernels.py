@@ -344,3 +344,67 @@ def test_grouped_query_blocks(case):
         errs.append(np.abs(o_g[b, rows, h].cpu().double().numpy() - ref))
     err = np.concatenate(errs)
     assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN
+
+
+# ------------------------------------------------------------- tiled forward
+# grid, tile, batch, heads, head_dim, dtype, mask (an STA window, or None: random per head)
+TILED_CASES = [
+    ((12, 16, 16), (6, 8, 8), 1, 2, 128, torch.bfloat16, (3, 3, 3)),   # 384-token tiles: 12-wave blocks
+    ((12, 64, 64), (1, 8, 8), 1, 2, 64, torch.bfloat16, None),         # 64-token tiles: grouped / key split
+    ((8, 8, 16), (4, 4, 4), 1, 3, 128, torch.bfloat16, None),          # th*tw = 16 divides 64
+    ((4, 32, 16), (2, 16, 8), 1, 2, 128, torch.bfloat16, (1, 3, 3)),   # 256-token tiles: 8-wave blocks
+    ((2, 4, 256), (1, 1, 128), 1, 2, 64, torch.bfloat16, (1, 1, 3)),   # tw a multiple of 64
+    ((4, 8, 8), (2, 4, 4), 2, 2, 64, torch.float32, None),             # fp32 path
+]
+
+
+@pytest.mark.parametrize("case", TILED_CASES, ids=[str(i) for i in range(len(TILED_CASES))])
+def test_tiled_attention(case):
+    """The forward on raster tokens with the tiles as blocks equals tile reorder ->
+    forward -> inverse reorder bit for bit (o and lse, grouped and not), and sampled
+    rows match the oracle."""
+    grid, tile, B, H, D, dtype, window = case
+    n, V = int(np.prod(grid)), int(np.prod(tile))
+    n_tiles = n // V
+    scale = D ** -0.5
+    q, k, v = (rand((B, n, H, D), dtype, 80 + i) for i in range(3))
+    if window is not None:
+        rp, ci = oracle.mask_sta(grid, tile, window)
+        slabs = 1
+    else:
+        slabs = B * H
+        rng = np.random.default_rng(84)
+        keep = rng.random((slabs * n_tiles, n_tiles)) < (0.4 if n_tiles < 100 else 0.1)
+        keep[np.arange(slabs * n_tiles), rng.integers(0, n_tiles, size=slabs * n_tiles)] = True
+        keep[2] = False                                           # an empty row
+        rp, ci = oracle.csr_from_bool(keep)
+    rpd, cid = torch.from_numpy(np.asarray(rp, np.int32)).to(DEV), torch.from_numpy(np.asarray(ci, np.int32)).to(DEV)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    # raster position of tile-major position p
+    perm = oracle.tile_reorder(np.arange(n).reshape(1, n, 1, 1), grid, tile)[0, :, 0, 0]
+    qt, kt, vt = (vsa.vsa_tile_reorder(x, grid, tile) for x in (qd, kd, vd))
+    if V == 64 and n_tiles >= 768:   # this case runs grouped
+        assert vsa.tiled_attn_workspace_bytes(qd, grid, tile, rpd, cid, slabs) > 0
+    for grouped in (True, False):
+        o_t, l_t = vsa.vsa_tiled_attn_fwd(qd, kd, vd, grid, tile, rpd, cid, slabs, scale, grouped=grouped)
+        o_r, l_r = vsa.vsa_block_sparse_attn_fwd(qt, kt, vt, rpd, cid, V, V, slabs, scale, grouped=grouped)
+        assert torch.equal(o_t, vsa.vsa_tile_reorder(o_r, grid, tile, inverse=True))
+        assert torch.equal(l_t[..., torch.from_numpy(perm).to(DEV)], l_r)
+    qn, kn, vn = (oracle.tile_reorder(to_np(x), grid, tile) for x in (q, k, v))
+    rng = np.random.default_rng(85)
+    errs = []
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        rows = np.concatenate([np.arange(min(V, 64)), rng.choice(n, 48, replace=False), [n - 1]])
+        base = 0 if slabs == 1 else (b * H + h) * n_tiles
+        ref, ref_lse = oracle.attention_rows(qn[b, rows, h], rows, kn[b, :, h], vn[b, :, h], rp, ci, base, V, V,
+                                             scale)
+        errs.append(np.abs(o_t[b, perm[rows], h].cpu().double().numpy() - ref))
+        got_lse = l_t[b, h, perm[rows]].cpu().double().numpy()
+        fin = np.isfinite(ref_lse)
+        assert np.array_equal(np.isfinite(got_lse), fin)
+        assert np.abs(got_lse[fin] - ref_lse[fin]).max() < (1e-4 if dtype == torch.float32 else 2e-2)
+    err = np.concatenate(errs)
+    if dtype == torch.float32:
+        assert err.max() <= F32_MAX
+    else:
+        assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN

@@ -1,7 +1,8 @@
 """GPU parity at the five workloads' full sizes, through the whole path.
 
 Each test runs the path the benchmark times (tile reorder -> mask -> attention ->
-inverse reorder) on the seeded synthetic inputs, compares the mask with the fp64
+inverse reorder; for the STA workloads the mask, then the attention with the reorder
+folded in, checked bit for bit against the separate passes) on the seeded synthetic inputs, compares the mask with the fp64
 oracle in full (bit-exact; NABLA / top-k rows whose decision sits within rounding
 of the cut are flagged, counted and exempt), and compares the output with the
 oracle fed the GPU's own mask: every row for the small workloads, 4,096 sampled
@@ -71,9 +72,15 @@ def _sampled_rows_check(name, x_cpu, o_gpu, rp, ci, block_q, block_k, n_slabs, p
     return err.max(), err.mean()
 
 
-def _run_path(x, grid, tile, mask_fn, block, n_slabs):
-    """reorder (if tiled) -> mask -> attention -> inverse reorder, on the GPU."""
+def _run_path(x, grid, tile, mask_fn, block, n_slabs, fused=False):
+    """reorder (if tiled) -> mask -> attention -> inverse reorder, on the GPU; fused: the
+    mask, then the attention on raster-order tokens with the reorder folded in."""
     qd, kd, vd = (x[w].to(DEV) for w in ("q", "k", "v"))
+    if fused:
+        rp, ci = mask_fn(None, None)
+        o, _ = vsa.vsa_tiled_attn_fwd(qd, kd, vd, grid, tile, rp, ci, n_slabs)
+        torch.cuda.synchronize()
+        return o, rp, ci
     if tile is not None:
         qd, kd, vd = (vsa.vsa_tile_reorder(t, grid, tile) for t in (qd, kd, vd))
     rp, ci = mask_fn(qd, kd)
@@ -125,7 +132,11 @@ def test_sta_workload():
     t0 = time.time()
     x = gen.make_inputs("sta")
     log(f"sta: inputs {time.time() - t0:.1f}s")
-    o, rp_d, ci_d = _run_path(x, grid, tile, lambda q, k: vsa.vsa_mask_sta(grid, tile, window, DEV), 384, 1)
+    mask = lambda q, k: vsa.vsa_mask_sta(grid, tile, window, DEV)
+    o, rp_d, ci_d = _run_path(x, grid, tile, mask, 384, 1, fused=True)
+    o_sep, _, _ = _run_path(x, grid, tile, mask, 384, 1)
+    assert torch.equal(o, o_sep)   # the folded reorder moves the same rows
+    del o_sep
     rp, ci = csr_np(rp_d, ci_d)
     orp, oci = oracle.mask_sta(grid, tile, window)
     assert np.array_equal(rp, orp) and np.array_equal(ci, oci) and len(ci) == 9152
@@ -216,8 +227,11 @@ def test_sta_heads_workload():
     wins = [cfg["windows"][h % len(cfg["windows"])] for h in range(H)]
     t0 = time.time()
     x = gen.make_inputs("sta_heads")
-    o, rp_d, ci_d = _run_path(x, grid, tile, lambda q, k: vsa.vsa_mask_sta_heads(grid, tile, wins, DEV),
-                              384, H)
+    mask = lambda q, k: vsa.vsa_mask_sta_heads(grid, tile, wins, DEV)
+    o, rp_d, ci_d = _run_path(x, grid, tile, mask, 384, H, fused=True)
+    o_sep, _, _ = _run_path(x, grid, tile, mask, 384, H)
+    assert torch.equal(o, o_sep)   # the folded reorder moves the same rows
+    del o_sep
     rp, ci = csr_np(rp_d, ci_d)
     orp, oci = oracle.mask_sta_heads(grid, tile, wins, 1)
     assert np.array_equal(rp, orp) and np.array_equal(ci, oci)
