@@ -147,18 +147,19 @@ __device__ inline bf16x8 frag(const uint16_t* tile, int row, int kd, int g) {
 }
 
 // A stream of 64-row tiles over a list of blocks (wave-uniform): block list[e], rows
-// [list[e] * bsz, min(+bsz, n)).
+// [list[e] * bsz, min(+bsz, n)).  Row indices fit 31 bits with 64 to spare (the call
+// checks), so the walk is 32-bit scalar arithmetic.
 struct Tiles {
   const int32_t* list;
   int e, e1;
-  int64_t r0, re;
+  int r0, re;
   int bsz;
-  int64_t n;
+  int n;
   __device__ bool valid() const { return e < e1; }
   __device__ void open() {
     if (e < e1) {
-      r0 = (int64_t)list[e] * bsz;
-      re = min(r0 + bsz, n);
+      r0 = list[e] * bsz;
+      re = bsz < n - r0 ? r0 + bsz : n;
     }
   }
   __device__ void next() {
@@ -199,11 +200,11 @@ struct CopyPlan {
       ch16[j] = 16u * ((l % SPR) ^ swz<D>(lrow[j]));
     }
   }
-  __device__ void issue(const uint16_t* abase, const uint16_t* bbase, int64_t r0, int64_t re, uint32_t row_bytes,
+  __device__ void issue(const uint16_t* abase, const uint16_t* bbase, int r0, int re, uint32_t row_bytes,
                         int row_stride, uint16_t* sa, uint16_t* sb, int w) const {
-    const char* at = (const char*)(abase + r0 * row_stride);
-    const char* bt = (const char*)(bbase + r0 * row_stride);
-    const int last = (int)min(re - r0, (int64_t)kT) - 1;
+    const char* at = (const char*)(abase + (int64_t)r0 * row_stride);
+    const char* bt = (const char*)(bbase + (int64_t)r0 * row_stride);
+    const int last = min(re - r0, kT) - 1;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int c = w + kNW * j;
@@ -375,7 +376,7 @@ __global__ __launch_bounds__(kNW * kWave, 2) void dq_kernel(
 
   const int64_t slab = n_slabs == 1 ? 0 : b * heads + h;
   const int64_t r = slab * wk.nb + qb;
-  Tiles it{col_idx, row_ptr[r], row_ptr[r + 1], 0, 0, block_k, nk};
+  Tiles it{col_idx, row_ptr[r], row_ptr[r + 1], 0, 0, block_k, (int)nk};
   it.open();
   const uint16_t* kbase = k + (b * nk * heads + h) * (int64_t)D;
   const uint16_t* vbase = v + (b * nk * heads + h) * (int64_t)D;
@@ -407,11 +408,13 @@ __global__ __launch_bounds__(kNW * kWave, 2) void dq_kernel(
   wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
 
+  // the tile after `it` is advanced one iteration ahead, after the products are issued, so
+  // the walk's scalar work is off the loop head where every wave meets after the barrier
+  Tiles nx = it;
+  nx.next();
   int buf = 0;
   while (it.valid()) {
-    const int valid = (int)min((int64_t)kT, it.re - it.r0);
-    Tiles nx = it;
-    nx.next();
+    const int valid = min(kT, it.re - it.r0);
     if (nx.valid()) plan.issue(kbase, vbase, nx.r0, nx.re, row_bytes, row_stride, sm.a[buf ^ 1], sm.b[buf ^ 1], w);
     const uint16_t* sk = sm.a[buf];
     const uint16_t* sv = sm.b[buf];
@@ -447,10 +450,13 @@ __global__ __launch_bounds__(kNW * kWave, 2) void dq_kernel(
       for (int t = 0; t < D / 32; ++t)
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[t], dsb[kk], acc[t], 0, 0, 0);
     }
+    Tiles nn = nx;
+    nn.next();
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     buf ^= 1;
     it = nx;
+    nx = nn;
   }
 
   if constexpr (KS == 2) {  // the key halves add
@@ -517,7 +523,7 @@ __global__ __launch_bounds__(kNW * kWave, 1) void dkdv_kernel(
 
   const int64_t slab = n_slabs == 1 ? 0 : b * heads + h;
   const int64_t c = slab * wk.nb + kb;
-  Tiles it{row_idx, col_ptr[c], col_ptr[c + 1], 0, 0, block_q, nq};
+  Tiles it{row_idx, col_ptr[c], col_ptr[c + 1], 0, 0, block_q, (int)nq};
   it.open();
   const uint16_t* qbase = q + (b * nq * heads + h) * (int64_t)D;
   const uint16_t* dobase = dout + (b * nq * heads + h) * (int64_t)D;
@@ -525,8 +531,8 @@ __global__ __launch_bounds__(kNW * kWave, 1) void dkdv_kernel(
   const float* dl_h = delta + (b * heads + h) * nq;
   const CopyPlan<D> plan(w, l);
   // wave 0 stages the tile's lse and D through registers (64 queries, one per lane)
-  auto fetch_ld = [&](int64_t r0, int64_t re, float& lv, float& dv_) {
-    const int64_t qq = r0 + l;
+  auto fetch_ld = [&](int r0, int re, float& lv, float& dv_) {
+    const int qq = r0 + l;
     lv = qq < re ? lse_h[qq] * kLog2e : INFINITY;
     dv_ = qq < re ? dl_h[qq] : 0.f;
   };
@@ -563,10 +569,11 @@ __global__ __launch_bounds__(kNW * kWave, 1) void dkdv_kernel(
   wait_vmcnt<0>();
   __syncthreads();
 
+  // the tile after `it` is advanced one iteration ahead (as in the dQ kernel)
+  Tiles nx = it;
+  nx.next();
   int buf = 0;
   while (it.valid()) {
-    Tiles nx = it;
-    nx.next();
     if (nx.valid()) {
       plan.issue(qbase, dobase, nx.r0, nx.re, row_bytes, row_stride, sm.a[buf ^ 1], sm.b[buf ^ 1], w);
       if (w == 0) fetch_ld(nx.r0, nx.re, lv, dv_);
@@ -618,10 +625,13 @@ __global__ __launch_bounds__(kNW * kWave, 1) void dkdv_kernel(
       sm.lse[buf ^ 1][l] = lv;
       sm.dl[buf ^ 1][l] = dv_;
     }
+    Tiles nn = nx;
+    nn.next();
     wait_vmcnt<0>();
     __syncthreads();
     buf ^= 1;
     it = nx;
+    nx = nn;
   }
 
   if constexpr (KS == 2) {  // the query halves add
