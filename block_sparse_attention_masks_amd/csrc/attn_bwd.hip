@@ -188,6 +188,10 @@ struct Work {
 // tensor a (c < CB) or b (c - CB) of a tile into LDS; rows past the last valid one repeat it.
 template <int D>
 struct CopyPlan {
+  // The same copy, with each lane's row and slot recomputed from the lane id (which the
+  // caller makes opaque, so the 2 NJ values are not kept live across the loop).
+  static __device__ void issue_lean(const uint16_t* abase, const uint16_t* bbase, int r0, int re,
+                                    uint32_t row_bytes, int row_stride, uint16_t* sa, uint16_t* sb, int w, int l);
   static constexpr int SPR = D / 8, RPC = 64 / SPR, CB = kT / RPC, NJ = (2 * CB + kNW - 1) / kNW;
   int lrow[NJ];
   uint32_t ch16[NJ];
@@ -201,7 +205,32 @@ struct CopyPlan {
     }
   }
   __device__ void issue(const uint16_t* abase, const uint16_t* bbase, int r0, int re, uint32_t row_bytes,
-                        int row_stride, uint16_t* sa, uint16_t* sb, int w) const {
+                        int row_stride, uint16_t* sa, uint16_t* sb, int w) const;
+};
+
+template <int D>
+__device__ void CopyPlan<D>::issue_lean(const uint16_t* abase, const uint16_t* bbase, int r0, int re,
+                                        uint32_t row_bytes, int row_stride, uint16_t* sa, uint16_t* sb, int w,
+                                        int l) {
+  const char* at = (const char*)(abase + (int64_t)r0 * row_stride);
+  const char* bt = (const char*)(bbase + (int64_t)r0 * row_stride);
+  const int last = min(re - r0, kT) - 1;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int c = w + kNW * j;
+    if (c < 2 * CB) {
+      const int cb = c < CB ? c : c - CB;
+      const int lrow = cb * RPC + l / SPR;
+      const uint32_t ro = __umul24((uint32_t)min(lrow, last), row_bytes) + 16u * ((l % SPR) ^ swz<D>(lrow));
+      if (c < CB) load_lds16((const uint16_t*)(at + ro), sa + c * 512);
+      else load_lds16((const uint16_t*)(bt + ro), sb + (c - CB) * 512);
+    }
+  }
+}
+
+template <int D>
+__device__ void CopyPlan<D>::issue(const uint16_t* abase, const uint16_t* bbase, int r0, int re, uint32_t row_bytes,
+                                   int row_stride, uint16_t* sa, uint16_t* sb, int w) const {
     const char* at = (const char*)(abase + (int64_t)r0 * row_stride);
     const char* bt = (const char*)(bbase + (int64_t)r0 * row_stride);
     const int last = min(re - r0, kT) - 1;
@@ -214,8 +243,7 @@ struct CopyPlan {
         else load_lds16((const uint16_t*)(bt + ro), sb + (c - CB) * 512);
       }
     }
-  }
-};
+}
 
 // ------------------------------------------------------------------ 1. D
 // One thread per 8 elements of a token row; the D / 8 lanes of a head reduce with DPP.
@@ -491,7 +519,7 @@ __global__ __launch_bounds__(kNW * kWave, 2) void dq_kernel(
 // A workgroup of 4 waves owns 32 * 4 / KS key rows of one key block; with KS = 2 the wave
 // pairs (w, w + 2) share 32 keys and split each query tile, adding their sums at the end.
 template <int D, int KS>
-__global__ __launch_bounds__(kNW * kWave, 1) void dkdv_kernel(
+__global__ __launch_bounds__(kNW * kWave, KS == 1 ? 2 : 1) void dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     float* __restrict__ dk, float* __restrict__ dv, int64_t nq, int64_t nk, int heads, int block_q, int block_k,
@@ -529,7 +557,15 @@ __global__ __launch_bounds__(kNW * kWave, 1) void dkdv_kernel(
   const uint16_t* dobase = dout + (b * nq * heads + h) * (int64_t)D;
   const float* lse_h = lse + (b * heads + h) * nq;
   const float* dl_h = delta + (b * heads + h) * nq;
-  const CopyPlan<D> plan(w, l);
+  // KS = 1 runs two waves per SIMD, so the kernel must fit 256 registers: the copy plan
+  // and the transposed-read offsets are remade from an opaque lane id where they are used
+  // (kept live across the loop they would cost 24 registers).  KS = 2 runs one wave per
+  // SIMD and lets the compiler keep them.
+  auto lane = [&]() {
+    int x = l;
+    if constexpr (KS == 1) asm volatile("" : "+v"(x));
+    return x;
+  };
   // wave 0 stages the tile's lse and D through registers (64 queries, one per lane)
   auto fetch_ld = [&](int r0, int re, float& lv, float& dv_) {
     const int qq = r0 + l;
@@ -551,7 +587,7 @@ __global__ __launch_bounds__(kNW * kWave, 1) void dkdv_kernel(
   }
   float lv = 0.f, dv_ = 0.f;
   if (it.valid()) {
-    plan.issue(qbase, dobase, it.r0, it.re, row_bytes, row_stride, sm.a[0], sm.b[0], w);
+    CopyPlan<D>::issue_lean(qbase, dobase, it.r0, it.re, row_bytes, row_stride, sm.a[0], sm.b[0], w, lane());
     if (w == 0) {
       fetch_ld(it.r0, it.re, lv, dv_);
       sm.lse[0][l] = lv;
@@ -564,8 +600,6 @@ __global__ __launch_bounds__(kNW * kWave, 1) void dkdv_kernel(
   for (int t = 0; t < D / 32; ++t)
 #pragma unroll
     for (int a = 0; a < 16; ++a) adk[t][a] = 0.f, adv[t][a] = 0.f;
-  uint32_t tlo[D / 32], thi[D / 32];
-  tr_offsets<D>(tlo, thi, l);
   wait_vmcnt<0>();
   __syncthreads();
 
@@ -575,7 +609,8 @@ __global__ __launch_bounds__(kNW * kWave, 1) void dkdv_kernel(
   int buf = 0;
   while (it.valid()) {
     if (nx.valid()) {
-      plan.issue(qbase, dobase, nx.r0, nx.re, row_bytes, row_stride, sm.a[buf ^ 1], sm.b[buf ^ 1], w);
+      CopyPlan<D>::issue_lean(qbase, dobase, nx.r0, nx.re, row_bytes, row_stride, sm.a[buf ^ 1], sm.b[buf ^ 1], w,
+                              lane());
       if (w == 0) fetch_ld(nx.r0, nx.re, lv, dv_);
     }
     const uint16_t* sq = sm.a[buf];
@@ -583,38 +618,57 @@ __global__ __launch_bounds__(kNW * kWave, 1) void dkdv_kernel(
 #pragma unroll
     for (int qs = 0; qs < NQS; ++qs) {
       const int q32 = 32 * (qh + qs);  // first query of this 32-query step within the tile
-      f32x16 s, dp;
+      // S, then P (fp32, kept in s) and its bf16 copy, then dV^T += dO^T P; rows past the
+      // tile's end have lse = +inf, so P = 0 there
+      f32x16 s;
 #pragma unroll
-      for (int a = 0; a < 16; ++a) s[a] = 0.f, dp[a] = 0.f;
+      for (int a = 0; a < 16; ++a) s[a] = 0.f;
 #pragma unroll
-      for (int kd = 0; kd < D / 16; ++kd) {
+      for (int kd = 0; kd < D / 16; ++kd)
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(sq, q32 + col, kd, g), kf[kd], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(sd, q32 + col, kd, g), vf[kd], dp, 0, 0, 0);
-      }
-      // P and dS over (query rows of this lane, its key); rows past the tile's end have
-      // lse = +inf, so P = 0 there
-      bf16x8 pb[2], db[2];
+      bf16x8 pb[2];
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
-        const int qr = q32 + 8 * a4 + 4 * g;
-        const f32x4 l4 = *(const f32x4*)&sm.lse[buf][qr];
-        const f32x4 d4 = *(const f32x4*)&sm.dl[buf][qr];
+        const f32x4 l4 = *(const f32x4*)&sm.lse[buf][q32 + 8 * a4 + 4 * g];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int a = 4 * a4 + i;
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[a], scale_log2, -l4[i]));
-          pb[a >> 3][a & 7] = (__bf16)p;
-          db[a >> 3][a & 7] = (__bf16)(p * (dp[a] - d4[i]));
+          s[a] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[a], scale_log2, -l4[i]));
+          pb[a >> 3][a & 7] = (__bf16)s[a];
         }
       }
-      // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per product, Q and dO read transposed
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         bf16x8 xt[D / 32];
+        uint32_t tlo[D / 32], thi[D / 32];
+        tr_offsets<D>(tlo, thi, lane());
         read_tr<D>(xt, tlo, thi, lds_addr(sd + (q32 + 16 * kk) * D));
 #pragma unroll
         for (int t = 0; t < D / 32; ++t)
           adv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xt[t], pb[kk], adv[t], 0, 0, 0);
+      }
+      // dP, then dS = P (dP - D), then dK^T += Q^T dS
+      f32x16 dp;
+#pragma unroll
+      for (int a = 0; a < 16; ++a) dp[a] = 0.f;
+#pragma unroll
+      for (int kd = 0; kd < D / 16; ++kd)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(sd, q32 + col, kd, g), vf[kd], dp, 0, 0, 0);
+      bf16x8 db[2];
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const f32x4 d4 = *(const f32x4*)&sm.dl[buf][q32 + 8 * a4 + 4 * g];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int a = 4 * a4 + i;
+          db[a >> 3][a & 7] = (__bf16)(s[a] * (dp[a] - d4[i]));
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 xt[D / 32];
+        uint32_t tlo[D / 32], thi[D / 32];
+        tr_offsets<D>(tlo, thi, lane());
         read_tr<D>(xt, tlo, thi, lds_addr(sq + (q32 + 16 * kk) * D));
 #pragma unroll
         for (int t = 0; t < D / 32; ++t)
