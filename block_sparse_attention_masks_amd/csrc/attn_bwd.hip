@@ -519,7 +519,7 @@ __global__ __launch_bounds__(kNW * kWave, 2) void dq_kernel(
 // A workgroup of 4 waves owns 32 * 4 / KS key rows of one key block; with KS = 2 the wave
 // pairs (w, w + 2) share 32 keys and split each query tile, adding their sums at the end.
 template <int D, int KS>
-__global__ __launch_bounds__(kNW * kWave, KS == 1 ? 2 : 1) void dkdv_kernel(
+__global__ __launch_bounds__(kNW * kWave, 2) void dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     float* __restrict__ dk, float* __restrict__ dv, int64_t nq, int64_t nk, int heads, int block_q, int block_k,
@@ -557,13 +557,14 @@ __global__ __launch_bounds__(kNW * kWave, KS == 1 ? 2 : 1) void dkdv_kernel(
   const uint16_t* dobase = dout + (b * nq * heads + h) * (int64_t)D;
   const float* lse_h = lse + (b * heads + h) * nq;
   const float* dl_h = delta + (b * heads + h) * nq;
-  // KS = 1 runs two waves per SIMD, so the kernel must fit 256 registers: the copy plan
-  // and the transposed-read offsets are remade from an opaque lane id where they are used
-  // (kept live across the loop they would cost 24 registers).  KS = 2 runs one wave per
-  // SIMD and lets the compiler keep them.
+  // Two waves per SIMD need the kernel within 256 registers: the copy plan and the
+  // transposed-read offsets are remade from an opaque lane id where they are used (kept
+  // live across the loop they would cost 24 registers).  KS = 1 then spills three dwords,
+  // reloaded once per tile; KS = 2 (its query-half merge adds to the pressure) spills a
+  // few fragments per tile, and still runs faster than at one wave per SIMD.
   auto lane = [&]() {
     int x = l;
-    if constexpr (KS == 1) asm volatile("" : "+v"(x));
+    asm volatile("" : "+v"(x));
     return x;
   };
   // wave 0 stages the tile's lse and D through registers (64 queries, one per lane)
