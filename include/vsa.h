@@ -16,6 +16,9 @@
  *   unless they went through vsa_tile_reorder.
  * - A block is a run of `block` consecutive tokens; the last block of a sequence
  *   may be ragged.  n_qblocks = ceil(nq / block_q), n_kblocks = ceil(nk / block_k).
+ * - Token counts (nq, nk, n) of the calls on token tensors must be below 2^31 - 64
+ *   (the kernels step through them in 31-bit arithmetic); larger ones give
+ *   VSA_ERR_SHAPE.
  * - CSR mask: row r lists, in ascending order, the key blocks kept by query block
  *   r; row_ptr[n_rows + 1] holds absolute int32 offsets into col_idx, both in
  *   device memory.  A mask shared by all (batch, head) has n_rows = n_qblocks
@@ -332,7 +335,7 @@ vsa_status vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v
  * multiple of 64 with tw dividing 64 or a multiple of 64, or th*tw dividing 64 (the
  * 6x8x8 and 1x8x8 tiles of the pages' video models qualify).
  * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE (non-positive sizes, T/H/W not divisible by
- * tt/th/tw, T*H*W >= 2^31), VSA_ERR_DTYPE, VSA_ERR_PARAM (n_slabs, scale),
+ * tt/th/tw, T*H*W >= 2^31 - 64), VSA_ERR_DTYPE, VSA_ERR_PARAM (n_slabs, scale),
  * VSA_ERR_UNSUPPORTED (head_dim not 64/128, misalignment, tile shape), VSA_ERR_HIP.
  */
 vsa_status vsa_tiled_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -132,6 +132,8 @@ def test_attn_validation(L):
     assert attn(L, dtype=7)[0] == E_DTYPE
     assert attn(L, D=32)[0] == E_UNSUP
     assert attn(L, nk=-1)[0] == E_SHAPE
+    assert attn(L, nk=2 ** 31 - 64)[0] == E_SHAPE       # token counts stay below 2^31 - 64
+    assert attn(L, nq=2 ** 31 - 64, bq=2 ** 20)[0] == E_SHAPE
     assert attn(L, bq=0)[0] == E_SHAPE
     assert attn(L, slabs=3)[0] == E_PARAM
     assert attn(L, scale=float("nan"))[0] == E_PARAM
