@@ -8,11 +8,15 @@
 // the B operand of S^T = K Q^T.  NW is 12 or 8 when the query block is a multiple
 // of 384 or 256 rows (one copy of each K/V tile then serves that many rows; the
 // bytes copied per flop, not their latency, are what the copies cost), else 4;
-// blocks of at most 64 rows split each tile's keys between two wave pairs.  The
-// kept key blocks are walked as one stream of 64-key tiles:
+// blocks of at most 64 rows split each tile's keys between two wave pairs, or,
+// grouped, several consecutive blocks of at most 128 rows share a workgroup and walk
+// the union of their kept key blocks (a wave computes only on its own block's).
+// The kept key blocks are walked as one stream of 64-key tiles:
 //   * tile t+1 is copied from HBM straight into the other half of a
 //     double-buffered LDS stage (global_load_lds, 16 bytes per lane, no staging
-//     registers) while tile t is computed; one wait + barrier per tile;
+//     registers) while tile t is computed; one wait + barrier per tile.  The walk
+//     (32-bit scalar arithmetic) is advanced one tile ahead, after the products are
+//     issued, to keep it off the loop head where every wave meets after the barrier;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (M = keys, N = queries, K = head
 //     dim): the accumulator gives each lane one query and 16 keys, so the row max
 //     and row sum are in-lane plus one exchange between the half-waves;
@@ -27,7 +31,9 @@
 //     4g..4g+3 and 8+4g..8+4g+3), so P feeds the product without any shuffle.
 // Ragged key tails are masked with -inf; query rows past the block or the
 // sequence are computed but never stored.  A row with no kept block writes 0
-// and lse = -inf.
+// and lse = -inf.  Tiled (TL): q, k, v, o and lse are in raster order of a 3D grid
+// whose tiles are the blocks; every row address goes through the tile-major
+// permutation (see Tiling below) instead of the tensors being reordered.
 //
 // fp32 path: the same definition evaluated with fp32 FMA on the vector units,
 // one thread per query row (used for small fp32 problems).
