@@ -96,8 +96,15 @@ def attn_kernel_name(D, block_q, grouped=False, batch=1, heads=1, n_qblocks=1, t
 
 
 def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source's code: comments and blank space are dropped, so the stored
+    traffic figure stays keyed to the code the counters measured."""
+    import re
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"//[^\n]*", "", text)
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"\s+", " ", text).strip()
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def cpu_baseline(x, cfg, target_s=12.0):
