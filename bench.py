@@ -76,12 +76,14 @@ def attn_flops(rp, ci, block_q, block_k, nq, nk, D, bh, n_slabs):
     return 4.0 * D * total * (bh if n_slabs == 1 else 1)
 
 
-def attn_kernel_name(D, block_q, grouped=False, batch=1, heads=1, n_qblocks=1, tiled=False):
+def attn_kernel_name(D, block_q, block_k, grouped=False, batch=1, heads=1, n_qblocks=1, tiled=False):
     """Label of the bf16 instantiation the library launches.  Query blocks of <= 128 rows
     are grouped (when the library asks for a workspace) into 12-, 8- or 4-wave
     workgroups, the first width whose group count keeps enough workgroups; otherwise it
-    picks a 4-wave key split (<= 64 rows) or 12-, 8- or 4-wave workgroups from block_q.  The last
-    flag: raster-order tokens with the tiles as blocks (the fused tile reorder)."""
+    picks a 4-wave key split (<= 64 rows) or 12-, 8- or 4-wave workgroups from block_q.  The
+    fifth flag: raster-order tokens with the tiles as blocks (the fused tile reorder); the
+    last number: stream tiles per LDS stage (two for grouped, untiled key blocks of <= 64)."""
+    tl = str(tiled).lower()
     if grouped:
         wpb = -(-block_q // 32)
         for nw in (12, 8, 4):
@@ -89,10 +91,11 @@ def attn_kernel_name(D, block_q, grouped=False, batch=1, heads=1, n_qblocks=1, t
             if nw % wpb or G < 2:
                 continue
             if batch * heads * -(-n_qblocks // G) >= (512 if nw == 4 else 256):
-                return f"attn_fwd_bf16_kernel<{D}, 1, {nw}, true, {str(tiled).lower()}>"
+                tw = 2 if nw >= 8 and block_k <= 64 and not tiled else 1
+                return f"attn_fwd_bf16_kernel<{D}, 1, {nw}, true, {tl}, {tw}>"
     ks = 2 if block_q <= 64 else 1
     nw = 4 if ks == 2 else (12 if block_q % 384 == 0 else (8 if block_q % 256 == 0 else 4))
-    return f"attn_fwd_bf16_kernel<{D}, {ks}, {nw}, false, {str(tiled).lower()}>"
+    return f"attn_fwd_bf16_kernel<{D}, {ks}, {nw}, false, {tl}, 1>"
 
 
 def source_hash(path):
@@ -449,7 +452,7 @@ def main():
                    "parallelism": "none (one GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": attn_kernel_name(path.D, path.bq, path.ws is not None, path.B, path.H, path.nbq,
+                     "traffic": traffic, "kernel": attn_kernel_name(path.D, path.bq, path.bk, path.ws is not None, path.B, path.H, path.nbq,
                                                                  path.fused),
                      "flops_per_launch": flops, "ms_per_launch": round(attn_ms, 4)},
         "cpu_baseline": cpu,

@@ -16,7 +16,10 @@
 //     double-buffered LDS stage (global_load_lds, 16 bytes per lane, no staging
 //     registers) while tile t is computed; one wait + barrier per tile.  The walk
 //     (32-bit scalar arithmetic) is advanced one tile ahead, after the products are
-//     issued, to keep it off the loop head where every wave meets after the barrier;
+//     issued, to keep it off the loop head where every wave meets after the barrier.
+//     Grouped walks of key blocks of <= 64 keys hold two tiles per stage (TW = 2),
+//     one wait + barrier per pair: consecutive tiles then belong to different blocks,
+//     and a wave whose block skips the first goes straight on to the second;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (M = keys, N = queries, K = head
 //     dim): the accumulator gives each lane one query and 16 keys, so the row max
 //     and row sum are in-lane plus one exchange between the half-waves;
@@ -262,20 +265,34 @@ __device__ inline void read_v_step<64>(bf16x8 (&vf)[2], uint32_t base, const int
   }
 }
 
-template <int D>
+// The two tiles after the next one, kept when a stage holds two tiles.
+template <int TW>
+struct Lookahead {
+  TileIter n2, n3;
+};
+template <>
+struct Lookahead<1> {};
+
+// LDS copy slots: two stages of TW stream tiles each.
+template <int D, int TW>
 struct Smem {
-  uint16_t k[2][kBN * D];
-  uint16_t v[2][kBN * D];
+  uint16_t k[2 * TW][kBN * D];
+  uint16_t v[2 * TW][kBN * D];
 };
 
-template <int D, int KS, int NW, bool GR, bool TL>
+template <int D, int KS, int NW, bool GR, bool TL, int TW>
 __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
     int64_t nq, int64_t nk, int heads, int block_q, int block_k,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int n_slabs,
     float scale_log2, Work wk, Groups gp, Tiling tg) {
-  __shared__ __attribute__((aligned(1024))) Smem<D> sm;
+  __shared__ __attribute__((aligned(1024))) Smem<D, TW> sm;
+  // TW = 2: two stream tiles per stage, so per wait and barrier.  That pays off for grouped
+  // blocks of 64 rows, where consecutive tiles belong to different key blocks and so often
+  // to different waves: a wave with nothing to do for the first tile goes on to the second
+  // instead of waiting at a barrier.
+  static_assert(TW == 1 || (GR && NW >= 8 && !TL), "two tiles per stage: grouped, untiled, 8 or 12 waves");
   static_assert(KS == 1 || NW == 4, "key split runs with 4 waves");
   static_assert(!GR || KS == 1, "grouped query blocks use whole tiles");
   constexpr int BM = 32 * NW / KS;
@@ -405,6 +422,11 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
     }
   }
   if (it.valid()) issue(it, 0);
+  if constexpr (TW == 2) {
+    TileIter t1 = it;
+    t1.next();
+    if (t1.valid()) issue(t1, 1);
+  }
 
   f32x16 acc_o[D / 32];
 #pragma unroll
@@ -429,12 +451,26 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
     if constexpr (TL) t_.next(tg);
     else t_.next();
   };
+  // TW = 2: tiles n2 and n3 follow nx; slots cycle 0..3, a stage holding slots (0, 1) or
+  // (2, 3), and the first tile of a stage copies the next two into the other stage
   TileIter nx = it;
   advance(nx);
+  [[maybe_unused]] Lookahead<TW> la;
+  if constexpr (TW == 2) {
+    la.n2 = nx;
+    la.n2.next();
+    la.n3 = la.n2;
+    la.n3.next();
+  }
   int buf = 0;
   while (it.valid()) {
     const int valid = min(kBN, it.ke - it.k0);
-    if (nx.valid()) issue(nx, buf ^ 1);
+    if constexpr (TW == 1) {
+      if (nx.valid()) issue(nx, buf ^ 1);
+    } else if ((buf & 1) == 0) {
+      if (la.n2.valid()) issue(la.n2, buf ^ 2);
+      if (la.n3.valid()) issue(la.n3, buf ^ 3);
+    }
     const uint16_t* sk = sm.k[buf];
     const uint16_t* sv = sm.v[buf];
     // grouped: a wave whose query block does not keep this key block only helps copy it
@@ -511,13 +547,27 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
         acc_o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t], pf[kk], acc_o[t], 0, 0, 0);
     }
     }
-    TileIter nn = nx;
-    advance(nn);
-    wait_vmcnt<0>();               // the next tile's loads have landed
-    __builtin_amdgcn_s_barrier();  // ... for everyone; this tile is no longer read
-    buf ^= 1;
-    it = nx;
-    nx = nn;
+    if constexpr (TW == 1) {
+      TileIter nn = nx;
+      advance(nn);
+      wait_vmcnt<0>();               // the next tile's loads have landed
+      __builtin_amdgcn_s_barrier();  // ... for everyone; this tile is no longer read
+      buf ^= 1;
+      it = nx;
+      nx = nn;
+    } else {
+      TileIter nn = la.n3;
+      nn.next();
+      if (buf & 1) {
+        wait_vmcnt<0>();               // the next stage's loads have landed
+        __builtin_amdgcn_s_barrier();  // ... for everyone; this stage is no longer read
+      }
+      buf = (buf + 1) & 3;
+      it = nx;
+      nx = la.n2;
+      la.n2 = la.n3;
+      la.n3 = nn;
+    }
   }
 
   // ---- epilogue
@@ -660,6 +710,7 @@ struct FwdPlan {
   bool grouped;
   int ks, nw, G, wpb, n_groups;
   size_t ws_bytes;
+  int tw = 1;  // stream tiles per LDS stage
 };
 
 FwdPlan plan_fwd(const AttnArgs& a, bool have_ws) {
@@ -681,7 +732,11 @@ FwdPlan plan_fwd(const AttnArgs& a, bool have_ws) {
       break;
     }
   }
-  if (p.grouped && have_ws) return p;
+  if (p.grouped && have_ws) {
+    // every tile its own block (see the kernel); the tiled kernels have no registers to spare
+    if (p.nw >= 8 && a.block_k <= kBN && !a.tiled) p.tw = 2;
+    return p;
+  }
   const bool want = p.grouped;
   p = FwdPlan{false, a.block_q <= kBM / 2 ? 2 : 1, 4, 1, 1, 0, want ? p.ws_bytes : 0};
   if (p.ks == 1) p.nw = a.block_q % 384 == 0 ? 12 : (a.block_q % 256 == 0 ? 8 : 4);
@@ -786,13 +841,17 @@ hipError_t launch_attn_fwd(const AttnArgs& a, void* workspace, size_t workspace_
     constexpr int D = decltype(dc)::value;
     constexpr bool TL = decltype(tc)::value;
     if (pl.grouped) {
-      if (pl.nw == 12) launch(attn_fwd_bf16_kernel<D, 1, 12, true, TL>);
-      else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<D, 1, 8, true, TL>);
-      else launch(attn_fwd_bf16_kernel<D, 1, 4, true, TL>);
-    } else if (pl.ks == 2) launch(attn_fwd_bf16_kernel<D, 2, 4, false, TL>);
-    else if (pl.nw == 12) launch(attn_fwd_bf16_kernel<D, 1, 12, false, TL>);
-    else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<D, 1, 8, false, TL>);
-    else launch(attn_fwd_bf16_kernel<D, 1, 4, false, TL>);
+      if constexpr (!TL) {
+        if (pl.tw == 2 && pl.nw == 12) return launch(attn_fwd_bf16_kernel<D, 1, 12, true, false, 2>);
+        if (pl.tw == 2) return launch(attn_fwd_bf16_kernel<D, 1, 8, true, false, 2>);
+      }
+      if (pl.nw == 12) launch(attn_fwd_bf16_kernel<D, 1, 12, true, TL, 1>);
+      else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<D, 1, 8, true, TL, 1>);
+      else launch(attn_fwd_bf16_kernel<D, 1, 4, true, TL, 1>);
+    } else if (pl.ks == 2) launch(attn_fwd_bf16_kernel<D, 2, 4, false, TL, 1>);
+    else if (pl.nw == 12) launch(attn_fwd_bf16_kernel<D, 1, 12, false, TL, 1>);
+    else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<D, 1, 8, false, TL, 1>);
+    else launch(attn_fwd_bf16_kernel<D, 1, 4, false, TL, 1>);
   };
   using D64 = std::integral_constant<int, 64>;
   using D128 = std::integral_constant<int, 128>;

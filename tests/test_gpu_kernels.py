@@ -308,6 +308,9 @@ GROUPED_CASES = [
     (1, 48, 128, 2000, 2048, 64, 64, 0.5, True),     # 12 waves, 6 blocks per group; last group partial
     (1, 48, 64, 2000, 1900, 128, 128, 0.6, False),   # 12 waves, 3 blocks per group; shared mask
     (2, 20, 128, 2048, 2048, 128, 64, 0.4, True),    # 8 waves, 2 blocks per group
+    # 64-key blocks and smaller: two stream tiles per LDS stage
+    (1, 48, 64, 1536, 1900, 64, 64, 0.5, True),      # 8 waves, 4 blocks per group; ragged last key block
+    (2, 48, 64, 2000, 1000, 64, 32, 0.5, False),     # 12 waves, 32-key blocks (half-filled tiles)
 ]
 
 
