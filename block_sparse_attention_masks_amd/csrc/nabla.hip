@@ -43,27 +43,47 @@ Layout layout(int64_t bh, int D, int64_t nbq, int64_t nbk) {
 }
 
 // ------------------------------------------------------------------- 1. pool
-__device__ inline void widen8(const uint4& u, double* out, bool bf16, const uint4* second) {
-  if (bf16) {
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      out[2 * i] = (double)__uint_as_float(w[i] << 16);
-      out[2 * i + 1] = (double)__uint_as_float(w[i] & 0xffff0000u);
-    }
-  } else {
-    const uint4 v = *second;
-    const uint32_t w[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) out[i] = (double)__uint_as_float(w[i]);
-  }
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16 bytes read once: a streaming (nontemporal) load, which does not displace cached
+// lines (≈8% faster for this single pass over Q and K than a plain load)
+__device__ inline uint4 load_stream(const uint8_t* p) {
+  const u32x4 r = __builtin_nontemporal_load((const u32x4*)p);
+  return uint4{r.x, r.y, r.z, r.w};
 }
 
+// 8 consecutive elements of a row widened to fp64: 16 bytes of bf16, or 32 of fp32.
+template <bool BF16>
+struct Vec8 {
+  uint4 a, c;
+  __device__ void load(const uint8_t* p) {
+    a = load_stream(p);
+    if constexpr (!BF16) c = load_stream(p + 16);
+  }
+  __device__ void add_to(double* acc) const {
+    if constexpr (BF16) {
+      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += (double)__uint_as_float(w[i] << 16);
+        acc[2 * i + 1] += (double)__uint_as_float(w[i] & 0xffff0000u);
+      }
+    } else {
+      const uint32_t w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += (double)__uint_as_float(w[i]);
+    }
+  }
+};
+
 // grid: x = query blocks then key blocks, y = column slices of 8*blockDim.x elements,
-// z = batch.  The host sizes blockDim.x so that the slices cover a row evenly.
+// z = batch.  The host sizes blockDim.x so that the slices cover a row evenly.  Each lane
+// keeps U rows' loads in flight; the element type is a template parameter so that the
+// bf16 kernel holds only its own registers (and so keeps enough waves resident).
 constexpr int kPoolMaxThreads = 512;
+template <bool BF16>
 __global__ __launch_bounds__(kPoolMaxThreads) void pool_kernel(const uint8_t* __restrict__ q,
-                                                        const uint8_t* __restrict__ k, int bf16,
+                                                        const uint8_t* __restrict__ k,
                                                         int64_t nq, int64_t nk, int bq, int bk,
                                                         int nbq, int nbk, int heads, int D,
                                                         double* __restrict__ qp,
@@ -79,36 +99,25 @@ __global__ __launch_bounds__(kPoolMaxThreads) void pool_kernel(const uint8_t* __
   const int hd = heads * D;
   const int vec = blockIdx.y * blockDim.x + threadIdx.x;  // 8-element vector index in a row
   if (vec * 8 >= hd) return;
-  const int esz = bf16 ? 2 : 4;
+  constexpr int esz = BF16 ? 2 : 4;
   const int64_t row_bytes = (int64_t)hd * esz;
   const int64_t t0 = (int64_t)blk * bsz, t1 = min(n, t0 + bsz);
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const uint8_t* p = src + (b * n + t0) * row_bytes + (int64_t)vec * 8 * esz;
   int64_t t = t0;
-  constexpr int U = 8;
+  constexpr int U = BF16 ? 16 : 8;
   for (; t + U <= t1; t += U) {
-    uint4 a[U], c[U];
+    Vec8<BF16> x[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      a[u] = *(const uint4*)(p + u * row_bytes);
-      if (!bf16) c[u] = *(const uint4*)(p + u * row_bytes + 16);
-    }
+    for (int u = 0; u < U; ++u) x[u].load(p + u * row_bytes);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      double x[8];
-      widen8(a[u], x, bf16, &c[u]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += x[i];
-    }
+    for (int u = 0; u < U; ++u) x[u].add_to(acc);
     p += U * row_bytes;
   }
   for (; t < t1; ++t) {
-    uint4 a = *(const uint4*)p, c = a;
-    if (!bf16) c = *(const uint4*)(p + 16);
-    double x[8];
-    widen8(a, x, bf16, &c);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += x[i];
+    Vec8<BF16> x;
+    x.load(p);
+    x.add_to(acc);
     p += row_bytes;
   }
   const double cnt = (double)(t1 - t0);
@@ -361,9 +370,9 @@ hipError_t launch_mask_nabla(const NablaArgs& a, hipStream_t stream) {
   const int per = (vpr + slices - 1) / slices;
   const int pool_threads = (per + kWave - 1) / kWave * kWave;
   dim3 g1(nbq + nbk, (vpr + pool_threads - 1) / pool_threads, (unsigned)a.batch);
-  hipLaunchKernelGGL(pool_kernel, g1, dim3(pool_threads), 0, stream, (const uint8_t*)a.q,
-                     (const uint8_t*)a.k, a.dtype == 1 ? 1 : 0, a.nq, a.nk, a.block_q, a.block_k,
-                     nbq, nbk, a.heads, a.head_dim, qp, kp);
+  hipLaunchKernelGGL(a.dtype == 1 ? pool_kernel<true> : pool_kernel<false>, g1, dim3(pool_threads), 0,
+                     stream, (const uint8_t*)a.q, (const uint8_t*)a.k, a.nq, a.nk, a.block_q,
+                     a.block_k, nbq, nbk, a.heads, a.head_dim, qp, kp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 

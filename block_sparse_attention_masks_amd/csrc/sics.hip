@@ -16,9 +16,18 @@
 namespace vsa {
 namespace {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16 bytes read once: a streaming (nontemporal) load, which does not displace cached lines
+__device__ inline uint4 load_stream(const uint8_t* p) {
+  const u32x4 r = __builtin_nontemporal_load((const u32x4*)p);
+  return uint4{r.x, r.y, r.z, r.w};
+}
+
 // 8 elements widened to fp64: the 16 bytes a (8 bf16) or a then c (8 fp32).
-__device__ inline void widen8(const uint4& a, const uint4& c, bool bf16, double* x) {
-  if (bf16) {
+template <bool BF16>
+__device__ inline void widen8(const uint4& a, const uint4& c, double* x) {
+  if constexpr (BF16) {
     const uint32_t w[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -65,9 +74,11 @@ __device__ inline double rsqrt_refined(double s) {
 constexpr int kVecs = 64;    // 8-element vectors of the row per workgroup
 constexpr int kPhases = 8;   // waves; wave p takes rows t0 + p, t0 + p + 8, ...
 
-// grid: x = blocks, y = groups of 64 vectors of the row, z = batch.  LANES = D / 8.
-template <int LANES>
-__global__ __launch_bounds__(kVecs * kPhases) void sics_kernel(const uint8_t* __restrict__ x, int bf16,
+// grid: x = blocks, y = groups of 64 vectors of the row, z = batch.  LANES = D / 8.  The
+// element type is a template parameter, so the bf16 kernel holds only its own registers;
+// rows are loaded U at a time and widened one at a time, as they are added.
+template <int LANES, bool BF16>
+__global__ __launch_bounds__(kVecs * kPhases) void sics_kernel(const uint8_t* __restrict__ x,
                                                                int64_t n, int block, int nb, int heads, int D,
                                                                double* __restrict__ out) {
   __shared__ double part[kPhases - 1][kVecs][8];
@@ -77,7 +88,7 @@ __global__ __launch_bounds__(kVecs * kPhases) void sics_kernel(const uint8_t* __
   const int l = threadIdx.x % kVecs, phase = threadIdx.x / kVecs;
   const int vec = blockIdx.y * kVecs + l;
   const bool live = vec * 8 < hd;  // a head's lanes are live or dead together
-  const int esz = bf16 ? 2 : 4;
+  constexpr int esz = BF16 ? 2 : 4;
   const int64_t row_bytes = (int64_t)hd * esz;
   const int64_t t0 = (int64_t)blk * block, t1 = min(n, t0 + block);
   const uint8_t* p = x + (b * n + t0 + phase) * row_bytes + (int64_t)(live ? vec : 0) * 8 * esz;
@@ -87,31 +98,40 @@ __global__ __launch_bounds__(kVecs * kPhases) void sics_kernel(const uint8_t* __
 #pragma unroll
     for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
     ss = row_sum<LANES>(ss);
-    const double inv = ss > 0 ? rsqrt_refined(ss) : 0.0;
+    // branch-free (a zero row gets weight 0): the estimate is made for every lane and kept
+    // opaque, so that the compiler does not turn the select into a branch per row, which
+    // would defer the accumulation and keep every row's widened values live
+    const bool nz = ss > 0;
+    double r = rsqrt_refined(nz ? ss : 1.0);
+    asm volatile("" : "+v"(r));
+    const double inv = nz ? r : 0.0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] += v[i] * inv;
   };
   // U rows in flight per lane
-  constexpr int U = 4;
+  constexpr int U = BF16 ? 8 : 4;
   const uint4 zero = {0, 0, 0, 0};
   int64_t t = t0 + phase;
   for (; t + (U - 1) * kPhases < t1; t += U * kPhases) {
-    double v[U][8];
+    uint4 a[U], c[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint4 a = live ? *(const uint4*)(p + u * kPhases * row_bytes) : zero;
-      const uint4 c = (live && !bf16) ? *(const uint4*)(p + u * kPhases * row_bytes + 16) : zero;
-      widen8(a, c, bf16, v[u]);
+      a[u] = load_stream(p + u * kPhases * row_bytes);
+      c[u] = BF16 ? zero : load_stream(p + u * kPhases * row_bytes + 16);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) add_row(v[u]);
+    for (int u = 0; u < U; ++u) {
+      double v[8];
+      widen8<BF16>(a[u], c[u], v);
+      add_row(v);
+    }
     p += U * kPhases * row_bytes;
   }
   for (; t < t1; t += kPhases) {
-    const uint4 a = live ? *(const uint4*)p : zero;
-    const uint4 c = (live && !bf16) ? *(const uint4*)(p + 16) : zero;
+    const uint4 a = load_stream(p);
+    const uint4 c = BF16 ? zero : load_stream(p + 16);
     double v[8];
-    widen8(a, c, bf16, v);
+    widen8<BF16>(a, c, v);
     add_row(v);
     p += kPhases * row_bytes;
   }
@@ -137,8 +157,10 @@ hipError_t launch_block_sics(const void* x, int bf16, int64_t batch, int heads, 
   const int nb = (int)((n + block - 1) / block);
   const int vpr = heads * D / 8;  // 8-element vectors per row
   const dim3 grid(nb, (vpr + kVecs - 1) / kVecs, (unsigned)batch);
-  hipLaunchKernelGGL(D == 64 ? sics_kernel<8> : sics_kernel<16>, grid, dim3(kVecs * kPhases), 0, stream,
-                     (const uint8_t*)x, bf16, n, block, nb, heads, D, scores);
+  auto kern = D == 64 ? (bf16 ? sics_kernel<8, true> : sics_kernel<8, false>)
+                      : (bf16 ? sics_kernel<16, true> : sics_kernel<16, false>);
+  hipLaunchKernelGGL(kern, grid, dim3(kVecs * kPhases), 0, stream, (const uint8_t*)x, n, block, nb, heads, D,
+                     scores);
   return hipGetLastError();
 }
 
