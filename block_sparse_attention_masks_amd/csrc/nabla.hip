@@ -245,19 +245,19 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
   }
   __syncthreads();
 
-  // Bitonic sort of (key, idx) into `before` order.
+  // Bitonic sort of (key, idx) into `before` order.  Each thread takes whole pairs: pair q
+  // of a stage joins i (q with a zero bit inserted at jj) and i + jj, so no lane idles.
   for (int kk = 2; kk <= SN; kk <<= 1) {
     for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      for (int i = t; i < SN; i += kThreads) {
-        const int p = i ^ jj;
-        if (p > i) {
-          const double ka = key[i], kb = key[p];
-          const int ia = idx[i], ib = idx[p];
-          const bool up = (i & kk) == 0;
-          if (up ? before(kb, ib, ka, ia) : before(ka, ia, kb, ib)) {
-            key[i] = kb; key[p] = ka;
-            idx[i] = ib; idx[p] = ia;
-          }
+      for (int q = t; q < SN / 2; q += kThreads) {
+        const int i = ((q & ~(jj - 1)) << 1) | (q & (jj - 1));
+        const int p = i + jj;
+        const double ka = key[i], kb = key[p];
+        const int ia = idx[i], ib = idx[p];
+        const bool up = (i & kk) == 0;
+        if (up ? before(kb, ib, ka, ia) : before(ka, ia, kb, ib)) {
+          key[i] = kb; key[p] = ka;
+          idx[i] = ib; idx[p] = ia;
         }
       }
       __syncthreads();
