@@ -198,69 +198,113 @@ __device__ double block_reduce(double x, bool is_max, double* red) {
   return r;
 }
 
-// dynamic LDS: double key[SN], int idx[SN], uint32 bits[words]
+// One compare-exchange of a bitonic stage, seen from one side: this element (k, i) at
+// position pos meets (pk, pi) at pos ^ jj; `up` sorts the kk-run ascending in `before`
+// order.  The lower position keeps the element that comes first, the upper the other.
+__device__ inline void keep_side(double& k, int& i, double pk, int pi, bool lower, bool up) {
+  const bool mine_first = before(k, i, pk, pi);
+  if (mine_first != (lower == up)) {
+    k = pk;
+    i = pi;
+  }
+}
+
+// E = SN / kThreads sort slots per thread: thread t holds positions t E .. t E + E - 1 in
+// registers.  A bitonic stage of distance jj pairs positions inside a thread (jj < E),
+// inside a wave (lanes jj / E apart, exchanged with shuffles) or across waves (through
+// LDS, the only stages that need a barrier: 3 of the 55 at SN = 1024).
+template <int E>
 __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restrict__ z, int nbk,
-                                                          int SN, double thr, int topk, Forced fc,
+                                                          double thr, int topk, Forced fc,
                                                           uint32_t* __restrict__ bitmap,
                                                           int32_t* __restrict__ row_ptr) {
-  extern __shared__ double smem[];
+  constexpr int SN = E * kThreads;
+  __shared__ double xkey[SN];
+  __shared__ int xidx[SN];
+  __shared__ uint32_t bits[SN / 32];
   __shared__ double red[kThreads / kWave];
   __shared__ double tsum[kThreads / kWave];
   __shared__ int cut_s;
-  double* key = smem;
-  int* idx = (int*)(key + SN);
   const int words = (nbk + 31) / 32;
-  uint32_t* bits = (uint32_t*)(idx + SN);
   const int64_t row = blockIdx.x;
   const double* zr = z + row * nbk;
   const int t = threadIdx.x;
+  const int i0 = t * E;  // this thread's first position
   for (int w = t; w < words; w += kThreads) bits[w] = 0;
   if (t == 0) cut_s = SN;
 
+  double key[E];
+  int idx[E];
   int n_cand = nbk;
   if (topk == 0) {
     double m = -DBL_MAX;
     for (int j = t; j < nbk; j += kThreads) m = fmax(m, zr[j]);
     m = block_reduce(m, true, red);
     double s = 0;
-    for (int j = t; j < nbk; j += kThreads) {
-      const double e = exp(zr[j] - m);
-      key[j] = e;
-      s += e;
-    }
-    s = block_reduce(s, false, red);   // contains a barrier: key[] is visible after it
-    for (int j = t; j < SN; j += kThreads) {
-      key[j] = j < nbk ? key[j] / s : -1.0;
-      idx[j] = j;
+    for (int j = t; j < nbk; j += kThreads) s += exp(zr[j] - m);
+    s = block_reduce(s, false, red);
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      const int j = i0 + r;
+      key[r] = j < nbk ? exp(zr[j] - m) / s : -1.0;
+      idx[r] = j;
     }
   } else {
-    n_cand = nbk;
     for (int r = 0; r < fc.n; ++r) n_cand -= fc.hi[r] - fc.lo[r];  // ranges are disjoint
-    for (int j = t; j < SN; j += kThreads) {
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      const int j = i0 + r;
       bool forced = false;
-      for (int r = 0; r < fc.n; ++r) forced |= (j >= fc.lo[r] && j < fc.hi[r]);
-      key[j] = (j < nbk && !forced) ? zr[j] : -DBL_MAX;
-      idx[j] = j;
+      for (int f = 0; f < fc.n; ++f) forced |= (j >= fc.lo[f] && j < fc.hi[f]);
+      key[r] = (j < nbk && !forced) ? zr[j] : -DBL_MAX;
+      idx[r] = j;
     }
   }
-  __syncthreads();
 
-  // Bitonic sort of (key, idx) into `before` order.  Each thread takes whole pairs: pair q
-  // of a stage joins i (q with a zero bit inserted at jj) and i + jj, so no lane idles.
+  // Bitonic sort of (key, idx) into `before` order.
+#pragma unroll
   for (int kk = 2; kk <= SN; kk <<= 1) {
+#pragma unroll
     for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      for (int q = t; q < SN / 2; q += kThreads) {
-        const int i = ((q & ~(jj - 1)) << 1) | (q & (jj - 1));
-        const int p = i + jj;
-        const double ka = key[i], kb = key[p];
-        const int ia = idx[i], ib = idx[p];
-        const bool up = (i & kk) == 0;
-        if (up ? before(kb, ib, ka, ia) : before(ka, ia, kb, ib)) {
-          key[i] = kb; key[p] = ka;
-          idx[i] = ib; idx[p] = ia;
+      if (jj < E) {
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+          if (r & jj) continue;
+          const int q = r + jj;
+          const bool up = ((i0 + r) & kk) == 0;
+          if (up ? before(key[q], idx[q], key[r], idx[r]) : before(key[r], idx[r], key[q], idx[q])) {
+            const double tk = key[r];
+            const int ti = idx[r];
+            key[r] = key[q];
+            idx[r] = idx[q];
+            key[q] = tk;
+            idx[q] = ti;
+          }
         }
+      } else if (jj < kWave * E) {
+        const int d = jj / E;  // lane distance
+        const bool lower = (lane_id() & d) == 0;
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+          const double pk = __shfl_xor(key[r], d, kWave);
+          const int pi = __shfl_xor(idx[r], d, kWave);
+          keep_side(key[r], idx[r], pk, pi, lower, ((i0 + r) & kk) == 0);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+          xkey[i0 + r] = key[r];
+          xidx[i0 + r] = idx[r];
+        }
+        __syncthreads();
+        const bool lower = (i0 & jj) == 0;  // jj >= kWave * E: the same for all r
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+          const int p = (i0 + r) ^ jj;
+          keep_side(key[r], idx[r], xkey[p], xidx[p], lower, ((i0 + r) & kk) == 0);
+        }
+        __syncthreads();
       }
-      __syncthreads();
     }
   }
 
@@ -269,11 +313,10 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
     if (thr >= 1.0) {
       n_keep = nbk;
     } else {
-      // Running sums of the sorted probabilities: each thread owns SN/kThreads
-      // consecutive entries.
-      const int per = SN / kThreads, i0 = t * per;
+      // Running sums of the sorted probabilities: each thread owns E consecutive entries.
       double local = 0;
-      for (int i = 0; i < per; ++i) local += (i0 + i < nbk) ? key[i0 + i] : 0.0;
+#pragma unroll
+      for (int r = 0; r < E; ++r) local += (i0 + r < nbk) ? key[r] : 0.0;
       // exclusive prefix of the per-thread totals: wave scan, then wave offsets
       double incl = local;
       const int ln = lane_id(), wv = t / kWave;
@@ -287,14 +330,15 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
       double before_sum = incl - local;
       for (int u = 0; u < wv; ++u) before_sum += tsum[u];
       double c = before_sum;
-      for (int i = 0; i < per; ++i) {
-        if (i0 + i >= nbk) break;
-        c += key[i0 + i];
-        if (c >= thr) {
-          atomicMin(&cut_s, i0 + i);
-          break;
+      int cut = SN;
+#pragma unroll
+      for (int r = 0; r < E; ++r) {
+        if (cut == SN && i0 + r < nbk) {
+          c += key[r];
+          if (c >= thr) cut = i0 + r;
         }
       }
+      if (cut < SN) atomicMin(&cut_s, cut);
       __syncthreads();
       n_keep = cut_s >= nbk ? nbk : cut_s + 1;
     }
@@ -303,10 +347,9 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
     for (int r = 0; r < fc.n; ++r)
       for (int j = fc.lo[r] + t; j < fc.hi[r]; j += kThreads) atomicOr(&bits[j >> 5], 1u << (j & 31));
   }
-  for (int i = t; i < n_keep; i += kThreads) {
-    const int j = idx[i];
-    atomicOr(&bits[j >> 5], 1u << (j & 31));
-  }
+#pragma unroll
+  for (int r = 0; r < E; ++r)
+    if (i0 + r < n_keep) atomicOr(&bits[idx[r] >> 5], 1u << (idx[r] & 31));
   __syncthreads();
   int cnt = 0;
   for (int w = t; w < words; w += kThreads) {
@@ -381,19 +424,19 @@ hipError_t launch_mask_nabla(const NablaArgs& a, hipStream_t stream) {
                      a.scale, z);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
-  int SN = kThreads;
-  while (SN < nbk) SN <<= 1;
+  int E = 1;  // sort slots per thread: SN = E * kThreads >= nbk (nbk <= 4096 is checked)
+  while (E * kThreads < nbk) E <<= 1;
   Forced fc{};
   fc.n = a.topk > 0 ? a.n_forced : 0;
   for (int r = 0; r < fc.n; ++r) {
     fc.lo[r] = a.forced[2 * r];
     fc.hi[r] = a.forced[2 * r + 1];
   }
-  const int words = (nbk + 31) / 32;
-  const size_t lds = (size_t)SN * (sizeof(double) + sizeof(int)) + words * sizeof(uint32_t);
   const int64_t rows = bh * nbq;
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)rows), dim3(kThreads), lds, stream, z, nbk, SN,
-                     a.threshold, a.topk, fc, bitmap, a.row_ptr);
+  auto sel = E == 1 ? select_kernel<1> : E == 2 ? select_kernel<2> : E == 4 ? select_kernel<4>
+           : E == 8 ? select_kernel<8> : select_kernel<16>;
+  hipLaunchKernelGGL(sel, dim3((unsigned)rows), dim3(kThreads), 0, stream, z, nbk, a.threshold, a.topk, fc,
+                     bitmap, a.row_ptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = launch_counts_to_offsets(a.row_ptr, rows, stream)) != hipSuccess) return e;
   hipLaunchKernelGGL(bitmap_fill_kernel, dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)),

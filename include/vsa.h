@@ -262,7 +262,7 @@ typedef struct {
  *           required size to *workspace_bytes and returns VSA_OK.
  * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE, VSA_ERR_DTYPE, VSA_ERR_PARAM,
  * VSA_ERR_CAPACITY (col_capacity or *workspace_bytes too small),
- * VSA_ERR_UNSUPPORTED (head_dim, alignment, n_kblocks > 8192), VSA_ERR_HIP.
+ * VSA_ERR_UNSUPPORTED (head_dim, alignment, n_kblocks > 4096), VSA_ERR_HIP.
  */
 vsa_status vsa_mask_nabla(const void* q, const void* k, int32_t dtype,
                           int64_t batch, int32_t heads, int32_t head_dim,
