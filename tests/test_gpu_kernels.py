@@ -111,6 +111,8 @@ def _compare_selected(rp, ci, orp, oci, exempt):
     (2048, 2048, 64, 64, 0.9, torch.float32), (1000, 777, 64, 32, 0.5, torch.bfloat16),
     (300, 4100, 50, 16, 0.95, torch.bfloat16), (129, 129, 128, 1, 0.7, torch.float32),
     (500, 500, 64, 64, 1.0, torch.bfloat16),
+    # rows longer than 1,024 and 2,048 blocks: 8 and 16 sort slots per thread
+    (130, 1500, 64, 1, 0.7, torch.bfloat16), (70, 4096, 64, 1, 0.5, torch.float32),
 ])
 def test_mask_nabla_bit_exact(nq, nk, bq, bk, thr, dtype):
     q = rand((1, nq, 3, 128), dtype, 2, 1.0)
@@ -125,14 +127,17 @@ def test_mask_nabla_bit_exact(nq, nk, bq, bk, thr, dtype):
     assert not bad, f"rows differing outside the flagged set: {bad[:10]}"
 
 
-def test_mask_topk_forced_bit_exact():
+@pytest.mark.parametrize("nk,bk,forced,topk", [
+    (3000, 64, [(0, 5), (40, 47)], 6),
+    (2000, 1, [(0, 25), (1900, 2000)], 16),     # 2,000 key blocks: 8 sort slots per thread
+])
+def test_mask_topk_forced_bit_exact(nk, bk, forced, topk):
     q = rand((2, 700, 2, 128), torch.bfloat16, 4)
-    k = rand((2, 3000, 2, 128), torch.bfloat16, 5)
-    forced = [(0, 5), (40, 47)]
-    rp, ci = csr_np(*vsa.vsa_mask_nabla(q.to(DEV), k.to(DEV), 64, 64, 0.1, topk=6, forced=forced))
-    orp, oci, ties = oracle.mask_ar(to_np(q), to_np(k), 64, 64, 0.1, 6, forced)
+    k = rand((2, nk, 2, 128), torch.bfloat16, 5)
+    rp, ci = csr_np(*vsa.vsa_mask_nabla(q.to(DEV), k.to(DEV), 64, bk, 0.1, topk=topk, forced=forced))
+    orp, oci, ties = oracle.mask_ar(to_np(q), to_np(k), 64, bk, 0.1, topk, forced)
     assert not _compare_selected(rp, ci, orp, oci, ties)
-    assert set(np.diff(rp).tolist()) == {18}
+    assert set(np.diff(rp).tolist()) == {sum(hi - lo for lo, hi in forced) + topk}
 
 
 # ------------------------------------------------------------------- attention
