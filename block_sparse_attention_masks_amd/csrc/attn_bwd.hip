@@ -29,6 +29,7 @@
 // row (dK, dV), lanes over head_dim (used for small fp32 problems).
 #include <math.h>
 
+#include "group_union.h"
 #include "vsa_internal.h"
 
 namespace vsa {
@@ -182,6 +183,15 @@ struct Smem {
 struct Work {
   int64_t items, per_xcd;
   int nb, mt_per_b;
+};
+
+// Grouped key blocks (dK, dV with blocks of <= 64 keys): G consecutive key blocks of a
+// slab share a 4-wave workgroup (wpb waves each) and walk the union of the query blocks
+// that keep any of them; list u = slab * n_groups + group holds cnt[u] entries at
+// idx[u * cap ..], each with a mask of the group's key blocks that it keeps.
+struct KeyGroups {
+  const int32_t *idx, *mask, *cnt;
+  int G, wpb, cap;
 };
 
 // Copy plan shared by both kernels: wave-load c = w + 4 j (c < 2 CB) moves RPC rows of
@@ -518,13 +528,17 @@ __global__ __launch_bounds__(kNW * kWave, 2) void dq_kernel(
 // ------------------------------------------------------------------ 4. dK, dV
 // A workgroup of 4 waves owns 32 * 4 / KS key rows of one key block; with KS = 2 the wave
 // pairs (w, w + 2) share 32 keys and split each query tile, adding their sums at the end.
-template <int D, int KS>
+// Grouped (GR): the 4 waves own gp.G key blocks of <= 64 keys (gp.wpb waves each) and walk
+// the union of their query blocks; a wave whose block is not kept by a tile's query block
+// only helps copy it.  One copy of Q and dO then serves 128 keys instead of 64.
+template <int D, int KS, bool GR>
 __global__ __launch_bounds__(kNW * kWave, 2) void dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     float* __restrict__ dk, float* __restrict__ dv, int64_t nq, int64_t nk, int heads, int block_q, int block_k,
     const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ row_idx, int n_slabs, float scale,
-    float scale_log2, Work wk) {
+    float scale_log2, Work wk, KeyGroups gp) {
+  static_assert(!GR || KS == 1, "grouped key blocks use whole query tiles");
   __shared__ __attribute__((aligned(1024))) Smem<D> sm;
   constexpr int BN = 32 * kNW / KS;
   constexpr int NQS = 2 / KS;  // 32-query steps of a tile per wave
@@ -533,25 +547,42 @@ __global__ __launch_bounds__(kNW * kWave, 2) void dkdv_kernel(
   if (item >= wk.items) return;
   const int mt = (int)(item % wk.mt_per_b);
   int64_t rest = item / wk.mt_per_b;
-  const int kb = (int)(rest % wk.nb);
+  const int kb = (int)(rest % wk.nb);  // key block, or group of key blocks
   rest /= wk.nb;
   const int h = (int)(rest % heads);
   const int64_t b = rest / heads;
-  const int64_t k_lo = (int64_t)kb * block_k + (int64_t)mt * BN;
-  const int64_t k_hi = min(min((int64_t)(kb + 1) * block_k, nk), k_lo + BN);
-  if (k_lo >= k_hi) return;
 
   const int l = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int col = l & 31, g = l >> 5;
-  const int kw = KS == 1 ? w : (w & 1);
+  const int kw = KS == 1 ? (GR ? 0 : w) : (w & 1);
   const int qh = KS == 1 ? 0 : (w >> 1);
   const int row_stride = heads * D;
   const uint32_t row_bytes = 2u * (uint32_t)row_stride;
 
+  // the workgroup's keys [k_lo, k_hi) -- grouped: this wave's 32 keys (possibly none)
+  int64_t k_lo, k_hi;
+  int lk = 0;  // grouped: the wave's key block within the group
+  if constexpr (GR) {
+    lk = w / gp.wpb;
+    const int64_t kbw = (int64_t)kb * gp.G + lk;
+    k_lo = kbw * block_k + (int64_t)(w % gp.wpb) * 32;
+    k_hi = min(min((kbw + 1) * block_k, nk), k_lo + 32);
+  } else {
+    k_lo = (int64_t)kb * block_k + (int64_t)mt * BN;
+    k_hi = min(min((int64_t)(kb + 1) * block_k, nk), k_lo + BN);
+    if (k_lo >= k_hi) return;
+  }
+
   const int64_t slab = n_slabs == 1 ? 0 : b * heads + h;
-  const int64_t c = slab * wk.nb + kb;
-  Tiles it{row_idx, col_ptr[c], col_ptr[c + 1], 0, 0, block_q, (int)nq};
+  Tiles it;
+  if constexpr (GR) {
+    const int64_t u = slab * wk.nb + kb;
+    it = Tiles{gp.idx, (int)(u * gp.cap), (int)(u * gp.cap) + gp.cnt[u], 0, 0, block_q, (int)nq};
+  } else {
+    const int64_t c = slab * wk.nb + kb;
+    it = Tiles{row_idx, col_ptr[c], col_ptr[c + 1], 0, 0, block_q, (int)nq};
+  }
   it.open();
   const uint16_t* qbase = q + (b * nq * heads + h) * (int64_t)D;
   const uint16_t* dobase = dout + (b * nq * heads + h) * (int64_t)D;
@@ -579,7 +610,9 @@ __global__ __launch_bounds__(kNW * kWave, 2) void dkdv_kernel(
   const bool ok = my_k < k_hi;
   bf16x8 kf[D / 16], vf[D / 16];
   {
-    const int64_t base = ((b * nk + (ok ? my_k : k_lo)) * heads + h) * D + 8 * g;
+    // a lane past the keys reads nothing; its address still names a row that exists (a
+    // grouped wave past the last key block has k_lo >= nk)
+    const int64_t base = ((b * nk + (ok ? my_k : (GR ? 0 : k_lo))) * heads + h) * D + 8 * g;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       kf[s] = __builtin_bit_cast(bf16x8, ok ? *(const u32x4*)(k + base + 16 * s) : u32x4{0, 0, 0, 0});
@@ -616,8 +649,10 @@ __global__ __launch_bounds__(kNW * kWave, 2) void dkdv_kernel(
     }
     const uint16_t* sq = sm.a[buf];
     const uint16_t* sd = sm.b[buf];
+    const bool member = !GR || ((gp.mask[it.e] >> lk) & 1);
 #pragma unroll
     for (int qs = 0; qs < NQS; ++qs) {
+      if (!member) break;
       const int q32 = 32 * (qh + qs);  // first query of this 32-query step within the tile
       // S, then P (fp32, kept in s) and its bf16 copy, then dV^T += dO^T P; rows past the
       // tile's end have lse = +inf, so P = 0 there
@@ -821,11 +856,35 @@ Work make_work(int64_t batch, int heads, int64_t n, int block, int rows_per_wg) 
 
 }  // namespace
 
+// Grouped dK, dV (bf16, key blocks of <= 64 keys): G = 4 / wpb key blocks per 4-wave
+// workgroup when that still leaves two workgroups per CU; G = 0 means ungrouped.
+struct KeyGroupPlan {
+  int G = 0, wpb = 1, n_groups = 0;
+  int64_t lists = 0;
+};
+
+KeyGroupPlan plan_key_groups(const AttnBwdArgs& a) {
+  KeyGroupPlan p;
+  const int64_t nbq = (a.nq + a.block_q - 1) / a.block_q, nbk = (a.nk + a.block_k - 1) / a.block_k;
+  if (a.dtype != 1 || a.block_k > 64) return p;
+  const int wpb = (a.block_k + 31) / 32, G = kNW / wpb;
+  const int64_t n_groups = (nbk + G - 1) / G;
+  const int64_t lists = (int64_t)a.n_slabs * n_groups;
+  if (a.batch * a.heads * n_groups < 512 || lists * nbq > 0x7fffffff) return p;
+  p.G = G;
+  p.wpb = wpb;
+  p.n_groups = (int)n_groups;
+  p.lists = lists;
+  return p;
+}
+
 size_t attn_bwd_workspace(const AttnBwdArgs& a) {
   const int64_t nbq = (a.nq + a.block_q - 1) / a.block_q, nbk = (a.nk + a.block_k - 1) / a.block_k;
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  const KeyGroupPlan kg = plan_key_groups(a);
   return al(4 * (size_t)(a.batch * a.heads * a.nq)) + al(4 * (size_t)(a.n_slabs * nbk)) +
-         al(4 * (size_t)(a.n_slabs * nbk + 1)) + al(4 * (size_t)(a.n_slabs * nbq * nbk));
+         al(4 * (size_t)(a.n_slabs * nbk + 1)) + al(4 * (size_t)(a.n_slabs * nbq * nbk)) +
+         (kg.G ? 2 * al(4 * (size_t)(kg.lists * nbq)) + al(4 * (size_t)kg.lists) : 0);
 }
 
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, void* workspace, hipStream_t stream) {
@@ -839,6 +898,16 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, void* workspace, hipStream_t st
   int32_t* col_ptr = (int32_t*)ws;
   ws += al(4 * (size_t)(a.n_slabs * nbk + 1));
   int32_t* row_idx = (int32_t*)ws;
+  ws += al(4 * (size_t)(a.n_slabs * nbq * nbk));
+  const KeyGroupPlan kg = plan_key_groups(a);
+  KeyGroups kgp{nullptr, nullptr, nullptr, 1, 1, 0};
+  if (kg.G) {
+    int32_t* gidx = (int32_t*)ws;
+    ws += al(4 * (size_t)(kg.lists * nbq));
+    int32_t* gmask = (int32_t*)ws;
+    ws += al(4 * (size_t)(kg.lists * nbq));
+    kgp = KeyGroups{gidx, gmask, (int32_t*)ws, kg.G, kg.wpb, nbq};
+  }
 
   const bool bf16 = a.dtype == 1;
   const int64_t rows = a.batch * a.nq;
@@ -875,7 +944,17 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, void* workspace, hipStream_t st
   const float sl2 = a.scale * kLog2e;
   const int ksq = a.block_q <= 64 ? 2 : 1, ksk = a.block_k <= 64 ? 2 : 1;
   const Work wq = make_work(a.batch, a.heads, a.nq, a.block_q, 32 * kNW / ksq);
-  const Work wkv = make_work(a.batch, a.heads, a.nk, a.block_k, 32 * kNW / ksk);
+  Work wkv = make_work(a.batch, a.heads, a.nk, a.block_k, 32 * kNW / ksk);
+  if (kg.G) {  // the union of each group's query blocks, from the CSC view
+    hipLaunchKernelGGL(group_union_kernel, dim3((unsigned)((kg.lists + kUnionWaves - 1) / kUnionWaves)),
+                       dim3(kUnionWaves * kWave), 0, stream, col_ptr, row_idx, nbk, kg.lists, kg.G, kg.n_groups,
+                       nbq, (int32_t*)kgp.idx, (int32_t*)kgp.mask, (int32_t*)kgp.cnt);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    wkv.nb = kg.n_groups;
+    wkv.mt_per_b = 1;
+    wkv.items = a.batch * a.heads * (int64_t)kg.n_groups;
+    wkv.per_xcd = (wkv.items + 7) / 8;
+  }
   auto lq = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3((unsigned)(wq.per_xcd * 8)), dim3(kNW * kWave), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
@@ -886,14 +965,16 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, void* workspace, hipStream_t st
     hipLaunchKernelGGL(kern, dim3((unsigned)(wkv.per_xcd * 8)), dim3(kNW * kWave), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
                        a.lse, delta, a.dk, a.dv, a.nq, a.nk, a.heads, a.block_q, a.block_k, col_ptr, row_idx,
-                       a.n_slabs, a.scale, sl2, wkv);
+                       a.n_slabs, a.scale, sl2, wkv, kgp);
   };
   if (a.head_dim == 64) {
     ksq == 2 ? lq(dq_kernel<64, 2>) : lq(dq_kernel<64, 1>);
-    ksk == 2 ? lk(dkdv_kernel<64, 2>) : lk(dkdv_kernel<64, 1>);
+    if (kg.G) lk(dkdv_kernel<64, 1, true>);
+    else ksk == 2 ? lk(dkdv_kernel<64, 2, false>) : lk(dkdv_kernel<64, 1, false>);
   } else {
     ksq == 2 ? lq(dq_kernel<128, 2>) : lq(dq_kernel<128, 1>);
-    ksk == 2 ? lk(dkdv_kernel<128, 2>) : lk(dkdv_kernel<128, 1>);
+    if (kg.G) lk(dkdv_kernel<128, 1, true>);
+    else ksk == 2 ? lk(dkdv_kernel<128, 2, false>) : lk(dkdv_kernel<128, 1, false>);
   }
   return hipGetLastError();
 }

@@ -44,6 +44,7 @@
 
 #include <type_traits>
 
+#include "group_union.h"
 #include "vsa_internal.h"
 
 namespace vsa {
@@ -666,43 +667,6 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
 }  // namespace
 
 namespace {
-
-// One wave per (slab, group): lane r < G walks row r of the group; each step takes the
-// smallest column any lane still holds (a wave minimum), records the lanes holding it as
-// the entry's mask, and advances them.  Lists are written at u * cap, their lengths to cnt.
-constexpr int kUnionWaves = 4;
-__global__ __launch_bounds__(kUnionWaves * kWave) void group_union_kernel(
-    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int nbq, int64_t n_lists, int G,
-    int n_groups, int cap, int32_t* __restrict__ gcol, int32_t* __restrict__ gmask, int32_t* __restrict__ gcnt) {
-  const int64_t u = (int64_t)blockIdx.x * kUnionWaves + threadIdx.x / kWave;
-  if (u >= n_lists) return;
-  const int l = lane_id();
-  const int64_t slab = u / n_groups;
-  const int qb = (int)(u % n_groups) * G + l;
-  int32_t e = 0, e1 = 0;
-  if (l < G && qb < nbq) {
-    e = row_ptr[slab * nbq + qb];
-    e1 = row_ptr[slab * nbq + qb + 1];
-  }
-  int32_t* oc = gcol + u * cap;
-  int32_t* om = gmask + u * cap;
-  int n = 0;
-  while (true) {
-    const int32_t val = e < e1 ? col_idx[e] : INT32_MAX;
-    int32_t m = val;
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) m = min(m, __shfl_xor(m, o, kWave));
-    if (m == INT32_MAX || n >= cap) break;  // cap: rows hold distinct columns below it
-    const uint64_t bits = __ballot(val == m);
-    if (l == 0) {
-      oc[n] = m;
-      om[n] = (int32_t)bits;
-    }
-    if (val == m) ++e;
-    ++n;
-  }
-  if (l == 0) gcnt[u] = n;
-}
 
 // How a call runs: grouped (wpb waves per query block, G blocks per workgroup of nw
 // waves), or per query block (ks = 2 key split for blocks <= 64 rows, else nw waves).

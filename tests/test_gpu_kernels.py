@@ -266,6 +266,10 @@ BWD_CASES = [
     (130, 700, 1, 128, 64, 48, 0.3, 1, torch.bfloat16),          # nq != nk
     (300, 300, 2, 64, 64, 64, 0.5, 2, torch.float32),
     (200, 333, 2, 128, 32, 48, 0.5, 1, torch.float32),
+    # grouped dK, dV (>= 512 groups): 2 key blocks of 64 per workgroup, per-head masks,
+    # a ragged last block alone in the last group; 4 blocks of 32 keys, shared mask
+    (128, 4150, 16, 64, 64, 64, 0.5, 16, torch.bfloat16),
+    (128, 2070, 32, 128, 64, 32, 0.5, 1, torch.bfloat16),
 ]
 # Normalised error bounds: |g - ref| over the reference's max (and mean) magnitude.  bf16:
 # P and dS are rounded to bf16 before the products (relative 2^-9 each) and D = sum dO * O
