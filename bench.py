@@ -21,15 +21,19 @@ roofline    = the attention kernel alone: the same FLOPs / its mean launch time
 speedup     = the same kernel on an all-ones mask (dense attention) / sparse.
 cpu_baseline= the fp64 oracle on a bounded sample (the same path for a subset of
               heads), FLOPs counted the same way (STA workload only).
+sclk        = the GFX clock (amdsmi, mean over the XCDs) while the attention kernel
+              runs back to back for --clock-s seconds after the timed steps; the
+              roofline's frac_at_measured_sclk scales the peak by it / 2.4 GHz.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sta]
-                       [--no-dense] [--no-cpu] [--no-bwd] [--unfused]
+                       [--no-dense] [--no-cpu] [--no-bwd] [--unfused] [--clock-s S]
 """
 import argparse
 import hashlib
 import json
 import os
 import sys
+import threading
 import time
 
 import numpy as np
@@ -108,6 +112,73 @@ def source_hash(path):
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     text = re.sub(r"\s+", " ", text).strip()
     return hashlib.sha256(text.encode()).hexdigest()[:16]
+
+
+class ClockSampler:
+    """Samples the graphics clock of the first GPU (amdsmi, current GFX clock in MHz) from a
+    background thread.  The published peaks assume 2.4 GHz; under a long matrix-core load the
+    clock runs lower, and the sampled clock says how much.  The firmware's reading lags the
+    load by some tens of milliseconds, so `result()` keeps the second half of the samples of
+    a window in which the load runs without a break.  Any failure (no amdsmi, no permission)
+    leaves the result's mean as None with the reason."""
+
+    SPEC_MHZ = 2400.0
+
+    def __init__(self, interval_s=0.01):
+        self.interval_s, self.samples, self.error = interval_s, [], None
+        self._stop, self._thread, self._amdsmi, self._handle = threading.Event(), None, None, None
+
+    def __enter__(self):
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._amdsmi = amdsmi
+            self._handle = amdsmi.amdsmi_get_processor_handles()[0]
+            self._read()  # fail here, not in the thread
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        except Exception as e:  # noqa: BLE001 -- reported, never fatal
+            self.error = f"{type(e).__name__}: {e}"[:200]
+        return self
+
+    def _read(self):
+        # the mean over the XCDs' current clocks (they differ by a few percent), else the
+        # first XCD's from the clock query
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
+        clks = [float(c) for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 65535]
+        if clks:
+            return sum(clks) / len(clks)
+        info = self._amdsmi.amdsmi_get_clock_info(self._handle, self._amdsmi.AmdSmiClkType.GFX)
+        return float(info["clk"])
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception as e:  # noqa: BLE001
+                self.error = f"{type(e).__name__}: {e}"[:200]
+                return
+            self._stop.wait(self.interval_s)
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+        if self._amdsmi is not None:
+            try:
+                self._amdsmi.amdsmi_shut_down()
+            except Exception:  # noqa: BLE001
+                pass
+        return False
+
+    def result(self, what):
+        kept = self.samples[len(self.samples) // 2:]
+        if not kept:
+            return {"mean_mhz": None, "error": self.error or "no samples"}
+        return {"mean_mhz": round(float(np.mean(kept)), 1), "min_mhz": round(min(kept), 1),
+                "max_mhz": round(max(kept), 1), "samples": len(kept),
+                "source": f"amdsmi: current GFX clock averaged over the XCDs of GPU 0, sampled every "
+                          f"{self.interval_s * 1e3:.0f} ms while {what}; second half of the samples"}
 
 
 def cpu_baseline(x, cfg, target_s=12.0):
@@ -290,6 +361,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--clock-s", type=float, default=1.5,
+                    help="seconds of back-to-back attention calls over which the GFX clock is sampled")
     ap.add_argument("--unfused", action="store_true",
                     help="sta / sta_heads: run the tile reorder as its own passes around the attention")
     args = ap.parse_args()
@@ -333,10 +406,24 @@ def main():
         all_marks.append(step(True))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
     for m in all_marks:
         for i, s in enumerate(stages):
             ev[s].append(m[i].elapsed_time(m[i + 1]))
     ms_step = wall * 1e3 / args.steps
+
+    # the clock the attention kernel runs at: sampled while it runs back to back for a while
+    # (enqueued ~50 ms at a time)
+    attn_fn = dict(stage_fns)["attn"]
+    n_inner = max(1, min(16, int(50.0 / max(float(np.mean(ev["attn"])), 1e-3))))
+    with ClockSampler() as clock:
+        t_end = time.perf_counter() + args.clock_s
+        while time.perf_counter() < t_end:
+            for _ in range(n_inner):
+                attn_fn()
+            torch.cuda.synchronize()
+    sclk = clock.result(f"the attention kernel ran back to back for {args.clock_s:.1f} s after the timed steps")
+    print(f"[bench] GFX clock under the attention kernel: {sclk}", file=sys.stderr, flush=True)
 
     rp_h = path.rp.cpu().numpy()
     ci_h = path.ci[: int(rp_h[-1])].cpu().numpy()
@@ -454,7 +541,12 @@ def main():
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": attn_kernel_name(path.D, path.bq, path.bk, path.ws is not None, path.B, path.H, path.nbq,
                                                                  path.fused),
-                     "flops_per_launch": flops, "ms_per_launch": round(attn_ms, 4)},
+                     "flops_per_launch": flops, "ms_per_launch": round(attn_ms, 4),
+                     # the same fraction against the peak scaled to the mean clock sampled in
+                     # the timed steps (the published peak assumes 2.4 GHz)
+                     "frac_at_measured_sclk": (None if sclk["mean_mhz"] is None else round(
+                         attn_tflops / (PEAK_BF16_TFLOPS * sclk["mean_mhz"] / ClockSampler.SPEC_MHZ), 4))},
+        "sclk": sclk,
         "cpu_baseline": cpu,
         "attn_tflops": round(attn_tflops, 2),
         "attn_pct_bf16_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
