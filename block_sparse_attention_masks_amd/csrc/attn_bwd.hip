@@ -14,6 +14,8 @@
 //                       S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T;
 //   4. dkdv_kernel      per key tile, over the query tiles of the blocks that keep
 //                       it: S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS.
+//                       Key blocks of <= 64 keys are grouped (group_union.h builds the
+//                       union of a group's query blocks from the CSC view first).
 // Every product is v_mfma_f32_32x32x16_bf16 on bf16 operands (P and dS rounded to
 // bf16), fp32 accumulation; gradients are written in fp32.
 //

@@ -364,8 +364,9 @@ vsa_status vsa_tiled_attn_fwd(const void* q, const void* k, const void* v, void*
  *          rows no kept pair touches get 0.
  * row_ptr/col_idx, n_slabs, scale: as for the forward.
  * workspace: device, 256-byte aligned; call with workspace = NULL to get the
- *          size in *workspace_bytes (fp32 D per query, and the transposed mask
- *          sized for n_slabs * n_qblocks * n_kblocks entries).
+ *          size in *workspace_bytes (fp32 D per query, the transposed mask sized
+ *          for n_slabs * n_qblocks * n_kblocks entries, and for bf16 key blocks of
+ *          <= 64 keys the union lists of the grouped dK/dV pass).
  * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE, VSA_ERR_DTYPE, VSA_ERR_PARAM (n_slabs,
  * scale), VSA_ERR_UNSUPPORTED (head_dim, alignment), VSA_ERR_CAPACITY
  * (workspace_bytes smaller than the query), VSA_ERR_HIP.
