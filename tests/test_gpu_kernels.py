@@ -206,6 +206,7 @@ def test_attention_deterministic_and_dense_mask():
     (2, 300, 3, 64, 7, torch.float32),
     (1, 130, 40, 128, 384, torch.bfloat16),     # one short block; 640 vectors per row -> two slices
     (1, 65, 1, 64, 1, torch.bfloat16),          # one-row blocks score 1
+    (1, 200, 5, 128, 33, torch.float32),        # fp32 at head_dim 128, ragged tail
 ])
 def test_block_sics_matches_oracle(B, N, H, D, block, dtype):
     x = rand((B, N, H, D), dtype, 31)
