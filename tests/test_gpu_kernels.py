@@ -271,6 +271,10 @@ BWD_CASES = [
     # a ragged last block alone in the last group; 4 blocks of 32 keys, shared mask
     (128, 4150, 16, 64, 64, 64, 0.5, 16, torch.bfloat16),
     (128, 2070, 32, 128, 64, 32, 0.5, 1, torch.bfloat16),
+    # many ragged 64-row query blocks with per-head masks (the key side too few to
+    # group); 128-row blocks on both sides
+    (4150, 256, 16, 64, 64, 64, 0.5, 16, torch.bfloat16),
+    (2100, 2100, 32, 128, 128, 128, 0.4, 1, torch.bfloat16),
 ]
 # Normalised error bounds: |g - ref| over the reference's max (and mean) magnitude.  bf16:
 # P and dS are rounded to bf16 before the products (relative 2^-9 each) and D = sum dO * O
