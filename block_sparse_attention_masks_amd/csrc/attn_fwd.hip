@@ -45,7 +45,7 @@
 #include <type_traits>
 
 #include "group_union.h"
-#include "vsa_internal.h"
+#include "/root/repo/block_sparse_attention_masks_amd/csrc/vsa_internal.h"
 
 namespace vsa {
 namespace {
@@ -370,17 +370,14 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
     const int k0 = t_.k0, ke = t_.ke;
     const int last = min(ke - k0, kBN) - 1;
     if constexpr (TL) {
-      // rows of a full copy tile: tile start + uniform part + lane part; a partial one
-      // (a tile shorter than 64 tokens) maps row by row, on a branch of its own
+      // rows of a copy tile: tile start + uniform part + lane part.  The lane part holds for
+      // every row the tile has, so a partial copy tile (the tail of a tile that is not a
+      // multiple of 64 tokens) takes it too; its rows past the last read the first row
+      // (finite values, masked out later)
       int rows[NJ];
-      if (last == kBN - 1) {
-        const int base_row = t_.rb + t_.uo;
+      const int base_row = t_.rb + t_.uo;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) rows[j] = base_row + loff[j];
-      } else {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) rows[j] = raster_row(tg, k0 + min(lrow[j], last));
-      }
+      for (int j = 0; j < NJ; ++j) rows[j] = base_row + (lrow[j] <= last ? loff[j] : 0);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int c = w + NW * j;
