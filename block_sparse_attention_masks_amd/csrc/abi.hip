@@ -265,7 +265,12 @@ vsa_status vsa_tiled_attn_fwd(const void* q, const void* k, const void* v, void*
   if (st != VSA_OK) return st;
   if (n_slabs != 1 && (int64_t)n_slabs != batch * heads) return VSA_ERR_PARAM;
   if (!(scale > 0.0f) || scale == INFINITY) return VSA_ERR_PARAM;
-  if (vsa::tiling_mode(th, tw) == 0) return VSA_ERR_UNSUPPORTED;
+  if (vsa::tiling_mode(th, tw) == 0 || block > 64 * vsa::kTiledMaxCopyTiles) return VSA_ERR_UNSUPPORTED;
+  // bf16: a copy tile's lane offsets (rows after its first token) are 24-bit rows and
+  // 32-bit bytes
+  const int64_t row_bytes = (int64_t)heads * head_dim * 2, span = vsa::tiling_lane_span(H, W, th, tw);
+  if (dtype == VSA_BF16 && (span >= (1 << 24) || row_bytes >= (1 << 24) || (span + 1) * row_bytes > (int64_t)UINT32_MAX))
+    return VSA_ERR_UNSUPPORTED;
   vsa::AttnArgs a{q, k, v, o, lse, dtype, batch, heads, head_dim, n, n, (int)block, (int)block,
                   row_ptr, col_idx, n_slabs, scale};
   a.tiled = 1;

@@ -45,7 +45,7 @@
 #include <type_traits>
 
 #include "group_union.h"
-#include "/root/repo/block_sparse_attention_masks_amd/csrc/vsa_internal.h"
+#include "vsa_internal.h"
 
 namespace vsa {
 namespace {
@@ -84,12 +84,13 @@ struct Groups {
 //   mode 1: P % 64 == 0 and tw | 64;  mode 2: P % 64 == 0 and 64 | tw;  mode 3: P | 64.
 struct Tiling {
   int H, W, tt, th, tw, NH, NW, P, V, HW, mode;
-  int dw, dh, dt;  // copy-tile advance in (w, h, t) within a tile: (0, 64 / tw, 0), (64, 0, 0)
-                   // or (0, 0, 64 / P) in modes 1, 2, 3
   // n / d = (n m) >> (31 + l) for n < 2^31, with l = ceil(log2 d) and m = ceil(2^(31 + l) / d)
   // (the round-up reciprocal of Granlund and Montgomery): for d = NH NW and d = NW
   uint32_t m_plane, m_nw;
   int l_plane, l_nw;
+  // uni(64 c) for the copy tiles c < ceil(V / 64) of a tile (V <= 64 kTiledMaxCopyTiles):
+  // a table in the kernel arguments, so the walk reads one value per copy tile
+  int uo_tab[kTiledMaxCopyTiles];
 };
 
 __device__ inline uint32_t div_magic(uint32_t n, uint32_t m, int l) {
@@ -131,9 +132,9 @@ struct TileIter {
   int block_k;
   int nk;
   int ks = 0;  // first key of the current block
-  // tiled: raster row of the block's first token, and the current copy tile's first row
-  // within the tile, (lt, lh, lw), with its raster offset uo = lt HW + lh W + lw
-  int rb = 0, lt = 0, lh = 0, lw = 0, uo = 0;
+  // tiled: raster row of the block's first token, and the uniform raster offset of the
+  // current copy tile within it
+  int rb = 0, uo = 0;
   __device__ bool valid() const { return e < e1; }
   __device__ void open() {  // position on the first tile of block col[e]
     if (e < e1) {
@@ -146,7 +147,7 @@ struct TileIter {
     open();
     if (e < e1) {
       rb = tile_start(t, col[e]);  // a block is a tile
-      lt = lh = lw = uo = 0;
+      uo = 0;
     }
   }
   __device__ void next() {
@@ -163,16 +164,8 @@ struct TileIter {
       open(t);
       return;
     }
-    // the next 64 rows of the same tile (only full copy tiles are followed by another):
-    // advance w, carry into h, carry into t; selects, no branches
-    lw += t.dw;
-    const int cw = lw >= t.tw;
-    lw -= cw * t.tw;
-    lh += t.dh + cw;
-    const int ch = lh >= t.th;
-    lh -= ch * t.th;
-    lt += t.dt + ch;
-    uo = lt * t.HW + lh * t.W + lw;
+    // the next 64 rows of the same tile: one scalar read of the table
+    uo = t.uo_tab[(k0 - ks) >> 6];
   }
 };
 
@@ -374,19 +367,20 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
       // every row the tile has, so a partial copy tile (the tail of a tile that is not a
       // multiple of 64 tokens) takes it too; its rows past the last read the first row
       // (finite values, masked out later)
-      int rows[NJ];
-      const int base_row = t_.rb + t_.uo;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) rows[j] = base_row + (lrow[j] <= last ? loff[j] : 0);
+      // the copy tile's first row is a scalar; the lane part is a 32-bit byte offset (the
+      // call checks that a copy tile's rows lie within 2^32 bytes and 2^24 rows of it)
+      const int64_t r0 = t_.rb + t_.uo;
+      const char* kt = (const char*)(kbase + r0 * row_stride);
+      const char* vt = (const char*)(vbase + r0 * row_stride);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int c = w + NW * j;
         if (c < 2 * CB) {
-          const uint64_t ro = (uint64_t)(uint32_t)rows[j] * row_bytes + ch16[j];
+          const uint32_t ro = __umul24((uint32_t)(lrow[j] <= last ? loff[j] : 0), row_bytes) + ch16[j];
           if (c < CB)
-            load_lds16((const uint16_t*)((const char*)kbase + ro), sm.k[stage] + c * 512);
+            load_lds16((const uint16_t*)(kt + ro), sm.k[stage] + c * 512);
           else
-            load_lds16((const uint16_t*)((const char*)vbase + ro), sm.v[stage] + (c - CB) * 512);
+            load_lds16((const uint16_t*)(vt + ro), sm.v[stage] + (c - CB) * 512);
         }
       }
     } else {
@@ -719,9 +713,17 @@ Tiling make_tiling(const AttnArgs& a) {
   t.V = a.tt * t.P;
   t.HW = a.H * a.W;
   t.mode = tiling_mode(a.th, a.tw);
-  t.dw = t.mode == 2 ? kBN : 0;
-  t.dh = t.mode == 1 ? kBN / a.tw : 0;
-  t.dt = t.mode == 3 ? kBN / t.P : 0;
+  // uni(r0) of copy tile r0 = 64 c: the raster offset of tile position r0 (its lane part
+  // is added per lane; in every supported mode the two add up for all 64 rows)
+  for (int c = 0; c < kTiledMaxCopyTiles; ++c) {
+    const int r = kBN * c;
+    if (r >= t.V) {
+      t.uo_tab[c] = 0;
+      continue;
+    }
+    const int lt = r / t.P, rr = r % t.P;
+    t.uo_tab[c] = lt * t.HW + (rr / t.tw) * t.W + rr % t.tw;
+  }
   auto magic = [](uint32_t d, uint32_t& m, int& l) {
     l = 0;
     while ((1ull << l) < d) ++l;
@@ -733,6 +735,16 @@ Tiling make_tiling(const AttnArgs& a) {
 }
 
 }  // namespace
+
+int64_t tiling_lane_span(int H, int W, int th, int tw) {
+  const int P = th * tw;
+  switch (tiling_mode(th, tw)) {
+    case 1: return (int64_t)(kBN / tw - 1) * W + tw - 1;
+    case 2: return kBN - 1;
+    case 3: return (int64_t)(kBN / P - 1) * H * W + (int64_t)(th - 1) * W + tw - 1;
+    default: return -1;
+  }
+}
 
 int tiling_mode(int th, int tw) {
   const int P = th * tw;

@@ -117,6 +117,12 @@ struct AttnArgs {
 // the tile's h-w plane must be a multiple of 64 tokens with tw dividing 64 or a multiple
 // of 64, or divide 64.
 int tiling_mode(int th, int tw);
+// The tiled forward walks at most this many 64-token copy tiles per tile (tiles of up to
+// 4096 tokens); larger tiles are not supported.
+constexpr int kTiledMaxCopyTiles = 64;
+// Largest lane part (rows after the copy tile's first token) of a 64-row copy tile of a
+// supported tile shape (-1 if unsupported); the bf16 kernel adds it as a 32-bit offset.
+int64_t tiling_lane_span(int H, int W, int th, int tw);
 // Workspace the bf16 forward uses for grouped query blocks (0 if none); without it the
 // call runs ungrouped.
 size_t attn_fwd_workspace(const AttnArgs& a);

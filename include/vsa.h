@@ -333,10 +333,15 @@ vsa_status vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v
  * workspace / workspace_bytes, scale: as for vsa_block_sparse_attn_fwd.
  * The tile's h-w plane must nest with the kernel's 64-token copy tile: th*tw a
  * multiple of 64 with tw dividing 64 or a multiple of 64, or th*tw dividing 64 (the
- * 6x8x8 and 1x8x8 tiles of the pages' video models qualify).
+ * 6x8x8 and 1x8x8 tiles of the pages' video models qualify), and a tile holds at
+ * most 4096 tokens.  For bf16 the 64 tokens of one copy tile must also lie within
+ * 2^24 rows and 4 GiB of the copy tile's first token: span < 2^24 and
+ * (span + 1) * heads * head_dim * 2 < 2^32, with span = (64/tw - 1) W + tw - 1, 63,
+ * or (64/(th tw) - 1) H W + (th - 1) W + tw - 1 for the three plane shapes above.
  * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE (non-positive sizes, T/H/W not divisible by
  * tt/th/tw, T*H*W >= 2^31 - 64), VSA_ERR_DTYPE, VSA_ERR_PARAM (n_slabs, scale),
- * VSA_ERR_UNSUPPORTED (head_dim not 64/128, misalignment, tile shape), VSA_ERR_HIP.
+ * VSA_ERR_UNSUPPORTED (head_dim not 64/128, misalignment, tile shape or size, copy-tile
+ * span), VSA_ERR_HIP.
  */
 vsa_status vsa_tiled_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                               int32_t dtype, int64_t batch, int32_t heads, int32_t head_dim,

@@ -168,6 +168,14 @@ def test_tiled_attn_validation(L):
     for grid, tile in (((12, 16, 16), (6, 8, 8)), ((2, 24, 32), (1, 12, 16)), ((2, 4, 256), (1, 1, 128)),
                        ((8, 8, 8), (4, 4, 4)), ((4, 4, 4), (1, 1, 1))):
         assert tiled(L, grid=grid, tile=tile, query=True)[0] == OK
+    # tiles of more than 4096 tokens
+    assert tiled(L, grid=(16, 16, 32), tile=(16, 16, 32), query=True)[0] == E_UNSUP
+    assert tiled(L, grid=(16, 16, 16), tile=(16, 16, 16), query=True)[0] == OK
+    # bf16 copy-tile lane offsets must fit 32-bit bytes and 24-bit rows: 1x1x1 tiles put a
+    # copy tile's 64 rows 64 planes apart (63 * 1024 * 1024 rows of 128 bytes > 4 GiB)
+    assert tiled(L, grid=(64, 1024, 1024), tile=(1, 1, 1), H=1, D=64)[0] == E_UNSUP
+    assert tiled(L, grid=(64, 256, 256), tile=(1, 1, 1), H=1, D=64, query=True)[0] == OK
+    assert tiled(L, grid=(64, 1024, 1024), tile=(1, 1, 1), H=1, D=64, dtype=0, query=True)[0] == OK  # fp32 path
     # workspace: none for 384-token tiles, the union lists for 64-token tiles (grouped)
     assert tiled(L, query=True) == (OK, 0)
     assert tiled(L, grid=(12, 64, 64), tile=(1, 8, 8), query=True)[1] > 0
