@@ -373,6 +373,7 @@ TILED_CASES = [
     ((2, 4, 256), (1, 1, 128), 1, 2, 64, torch.bfloat16, (1, 1, 3)),   # tw a multiple of 64
     ((6, 8, 8), (3, 4, 4), 1, 2, 128, torch.bfloat16, None),           # 48-token tiles: one partial copy tile each
     ((12, 8, 16), (6, 4, 4), 2, 2, 64, torch.bfloat16, (3, 1, 3)),     # 96-token tiles: a full and a partial copy tile
+    ((16, 16, 32), (16, 16, 16), 1, 2, 128, torch.bfloat16, None),     # 4,096-token tiles: all 64 copy-tile offsets
     ((4, 8, 8), (2, 4, 4), 2, 2, 64, torch.float32, None),             # fp32 path
 ]
 
