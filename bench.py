@@ -129,16 +129,10 @@ class ClockSampler:
         self._stop, self._thread, self._amdsmi, self._handle = threading.Event(), None, None, None
 
     def __enter__(self):
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            self._amdsmi = amdsmi
-            self._handle = amdsmi.amdsmi_get_processor_handles()[0]
-            self._read()  # fail here, not in the thread
-            self._thread = threading.Thread(target=self._run, daemon=True)
-            self._thread.start()
-        except Exception as e:  # noqa: BLE001 -- reported, never fatal
-            self.error = f"{type(e).__name__}: {e}"[:200]
+        # amdsmi is opened, read and closed on the sampling thread, so that a stuck driver
+        # query can only lose the reading, never hold up the benchmark
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
         return self
 
     def _read(self):
@@ -152,23 +146,32 @@ class ClockSampler:
         return float(info["clk"])
 
     def _run(self):
-        while not self._stop.is_set():
-            try:
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+        except Exception as e:  # noqa: BLE001 -- reported, never fatal
+            self.error = f"{type(e).__name__}: {e}"[:200]
+            return
+        self._amdsmi = amdsmi
+        try:
+            self._handle = amdsmi.amdsmi_get_processor_handles()[0]
+            while not self._stop.is_set():
                 self.samples.append(self._read())
-            except Exception as e:  # noqa: BLE001
-                self.error = f"{type(e).__name__}: {e}"[:200]
-                return
-            self._stop.wait(self.interval_s)
+                self._stop.wait(self.interval_s)
+        except Exception as e:  # noqa: BLE001
+            self.error = f"{type(e).__name__}: {e}"[:200]
+        finally:
+            try:
+                amdsmi.amdsmi_shut_down()
+            except Exception:  # noqa: BLE001
+                pass
 
     def __exit__(self, *exc):
         self._stop.set()
         if self._thread is not None:
-            self._thread.join()
-        if self._amdsmi is not None:
-            try:
-                self._amdsmi.amdsmi_shut_down()
-            except Exception:  # noqa: BLE001
-                pass
+            self._thread.join(timeout=5.0)
+            if self._thread.is_alive():
+                self.error = "amdsmi did not answer within 5 s"
         return False
 
     def result(self, what):
