@@ -370,8 +370,8 @@ def main():
                     help="sta / sta_heads: run the tile reorder as its own passes around the attention")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the path shards by head "
-              "with no communication and multi-GPU runs are not part of this build.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the path would shard by "
+              "head with no communication, and no multi-GPU run is implemented.", file=sys.stderr)
         sys.exit(2)
 
     from workloads import gen
