@@ -205,6 +205,29 @@ def test_select_golden(golden_dir):
         assert list(kept) == c["kept"], c
 
 
+def test_nabla_map_golden(golden_dir):
+    """The whole NABLA step on a hand-worked case (pool -> map scaled by 1/sqrt(D) ->
+    softmax over each row -> CDF cut): the pooled means exactly, and the CSR at two
+    thresholds chosen so that a softmax over the wrong axis, a 1/D scale or no scale each
+    keep other blocks."""
+    with open(os.path.join(golden_dir, "nabla_hand.json")) as f:
+        g = json.load(f)
+    D = g["head_dim"]
+    assert g["scale"] == D ** -0.5
+    qt = np.array(g["q_tokens"], np.float64)
+    kt = np.array(g["k_tokens"], np.float64)
+    assert np.array_equal(oracle.pool_blocks(qt, g["block_q"]), np.array(g["q_pooled"], np.float64))
+    assert np.array_equal(oracle.pool_blocks(kt, g["block_k"]), np.array(g["k_pooled"], np.float64))
+    q, k = qt[None, :, None, :], kt[None, :, None, :]          # [B=1, N, heads=1, D]
+    for c in g["cases"]:
+        rp, ci, flagged, near_tie = oracle.mask_nabla(q, k, g["block_q"], g["block_k"], g["scale"], c["thr"])
+        assert rows_of(rp, ci) == c["kept"], c
+        assert not flagged.any()
+        for mistake in g["plausible_mistakes"].values():   # the case separates the readings
+            if isinstance(mistake, dict):
+                assert mistake[str(c["thr"])] != c["kept"]
+
+
 def _random_row(rng, n):
     z = rng.standard_normal(n) * rng.uniform(0.1, 3.0)
     p = np.exp(z - z.max())
