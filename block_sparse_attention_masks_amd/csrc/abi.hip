@@ -17,6 +17,11 @@ vsa_status from_hip(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_HI
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// The bf16 attention kernels address the rows of a 64-key tile as a 24-bit row index
+// times a 24-bit row size: a token row (heads * head_dim bf16 values) must stay below
+// 2^24 bytes.
+bool bf16_rows_fit(int32_t heads, int32_t head_dim) { return (int64_t)heads * head_dim * 2 < (1 << 24); }
+
 // Common checks of a token-tensor problem (dtype, head_dim, sizes).
 vsa_status check_tokens(int32_t dtype, int64_t batch, int32_t heads, int32_t head_dim, int64_t nq,
                         int64_t nk, int32_t block_q, int32_t block_k) {
@@ -237,6 +242,7 @@ vsa_status vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v
   if (st != VSA_OK) return st;
   if (n_slabs != 1 && (int64_t)n_slabs != batch * heads) return VSA_ERR_PARAM;
   if (!(scale > 0.0f) || scale == INFINITY) return VSA_ERR_PARAM;
+  if (dtype == VSA_BF16 && !bf16_rows_fit(heads, head_dim)) return VSA_ERR_UNSUPPORTED;
   vsa::AttnArgs a{q, k, v, o, lse, dtype, batch, heads, head_dim, nq, nk, block_q, block_k,
                   row_ptr, col_idx, n_slabs, scale};
   const size_t want = dtype == VSA_BF16 ? vsa::attn_fwd_workspace(a) : 0;
@@ -269,7 +275,7 @@ vsa_status vsa_tiled_attn_fwd(const void* q, const void* k, const void* v, void*
   // bf16: a copy tile's lane offsets (rows after its first token) are 24-bit rows and
   // 32-bit bytes
   const int64_t row_bytes = (int64_t)heads * head_dim * 2, span = vsa::tiling_lane_span(H, W, th, tw);
-  if (dtype == VSA_BF16 && (span >= (1 << 24) || row_bytes >= (1 << 24) || (span + 1) * row_bytes > (int64_t)UINT32_MAX))
+  if (dtype == VSA_BF16 && (span >= (1 << 24) || !bf16_rows_fit(heads, head_dim) || (span + 1) * row_bytes > (int64_t)UINT32_MAX))
     return VSA_ERR_UNSUPPORTED;
   vsa::AttnArgs a{q, k, v, o, lse, dtype, batch, heads, head_dim, n, n, (int)block, (int)block,
                   row_ptr, col_idx, n_slabs, scale};
@@ -303,6 +309,7 @@ vsa_status vsa_block_sparse_attn_bwd(const void* q, const void* k, const void* v
   if (!(scale > 0.0f) || scale == INFINITY) return VSA_ERR_PARAM;
   const int64_t nbq = ceil_div(nq, block_q), nbk = ceil_div(nk, block_k);
   if ((int64_t)n_slabs * nbq * nbk > kI32Max || batch * heads * nq > kI32Max) return VSA_ERR_SHAPE;
+  if (dtype == VSA_BF16 && !bf16_rows_fit(heads, head_dim)) return VSA_ERR_UNSUPPORTED;
   vsa::AttnBwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, dtype, batch, heads, head_dim, nq, nk, block_q, block_k,
                      row_ptr, col_idx, n_slabs, scale};
   const size_t need = vsa::attn_bwd_workspace(a);

@@ -298,8 +298,10 @@ vsa_status vsa_mask_nabla(const void* q, const void* k, int32_t dtype,
  * result bit for bit for query blocks of 65 to 128 rows; ungrouped blocks of at most
  * 64 rows split each key tile between two waves and add their halves at the end, so
  * there the two agree to rounding only.
+ * bf16 token rows must be below 2^24 bytes (heads * head_dim * 2 < 2^24, i.e. at most
+ * 65,535 heads at head_dim 128); the kernels address a tile's rows in 24-bit arithmetic.
  * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE, VSA_ERR_DTYPE, VSA_ERR_PARAM (n_slabs, scale),
- * VSA_ERR_UNSUPPORTED (head_dim not 64/128, misalignment), VSA_ERR_CAPACITY,
+ * VSA_ERR_UNSUPPORTED (head_dim not 64/128, misalignment, bf16 row size), VSA_ERR_CAPACITY,
  * VSA_ERR_HIP.  The CSR contents are trusted: column indices must lie in
  * [0, n_kblocks) and row_ptr must be non-decreasing.
  */
@@ -372,8 +374,9 @@ vsa_status vsa_tiled_attn_fwd(const void* q, const void* k, const void* v, void*
  *          size in *workspace_bytes (fp32 D per query, the transposed mask sized
  *          for n_slabs * n_qblocks * n_kblocks entries, and for bf16 key blocks of
  *          <= 64 keys the union lists of the grouped dK/dV pass).
+ * bf16 token rows must be below 2^24 bytes, as for the forward.
  * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE, VSA_ERR_DTYPE, VSA_ERR_PARAM (n_slabs,
- * scale), VSA_ERR_UNSUPPORTED (head_dim, alignment), VSA_ERR_CAPACITY
+ * scale), VSA_ERR_UNSUPPORTED (head_dim, alignment, bf16 row size), VSA_ERR_CAPACITY
  * (workspace_bytes smaller than the query), VSA_ERR_HIP.
  */
 vsa_status vsa_block_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,

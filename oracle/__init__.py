@@ -33,7 +33,8 @@ Where the pages leave a step open, the reading taken is stated in the function.
 from .reorder import tile_reorder, tile_order_source  # noqa: F401
 from .masks import (  # noqa: F401
     csr_from_bool, csr_to_bool, mask_all, mask_sta, mask_radial, radial_keep_tokens,
-    pool_blocks, nabla_select_row, mask_nabla, ar_forced_ranges, ar_select_row, mask_ar,
+    pool_blocks, nabla_select_row, mask_nabla, ar_forced_ranges, ar_select_row, mask_ar, pooled_maps,
+    nabla_cut_admissible, topk_admissible, forced_flags,
     mask_sta_heads, mask_union, csr_concat,
 )
 from .attention import (  # noqa: F401

@@ -206,6 +206,21 @@ def _pooled_logits(qh, kh, block_q, block_k, scale):
     return (pool_blocks(qh, block_q) @ pool_blocks(kh, block_k).T) * scale
 
 
+def pooled_maps(q, k, block_q, block_k, scale, softmax):
+    """The pooled map of every (batch, head), in (b, h) order: Z = pool(Q) pool(K)^T *
+    scale, or with softmax=True its row softmax p (one distribution over the key blocks
+    per query block).  NABLA explainer (aibr.jp/archives/124678), sec. 3."""
+    B, _, Hh, _ = q.shape
+    for b in range(B):
+        for h in range(Hh):
+            z = _pooled_logits(np.asarray(q[b, :, h, :], np.float64),
+                               np.asarray(k[b, :, h, :], np.float64), block_q, block_k, scale)
+            if softmax:
+                p = np.exp(z - z.max(axis=1, keepdims=True))
+                z = p / p.sum(axis=1, keepdims=True)
+            yield z
+
+
 def mask_nabla(q, k, block_q, block_k, scale, thr):
     """NABLA mask per (batch, head).
 
@@ -217,24 +232,39 @@ def mask_nabla(q, k, block_q, block_k, scale, thr):
     q: [B, Nq, Hh, D], k: [B, Nk, Hh, D] (fp64 or anything numpy upcasts).
     Returns (row_ptr, col_idx, flagged bool[rows], near_tie bool[rows]) with rows
     ordered (b, h, qblock)."""
-    B, _, Hh, _ = q.shape
     nbk = -(-k.shape[1] // block_k)
     keeps, flags, ties = [], [], []
-    for b in range(B):
-        for h in range(Hh):
-            z = _pooled_logits(np.asarray(q[b, :, h, :], np.float64),
-                               np.asarray(k[b, :, h, :], np.float64), block_q, block_k, scale)
-            p = np.exp(z - z.max(axis=1, keepdims=True))
-            p = p / p.sum(axis=1, keepdims=True)
-            for row in p:
-                kept, fl, nt = nabla_select_row(row, thr)
-                m = np.zeros(nbk, dtype=bool)
-                m[kept] = True
-                keeps.append(m)
-                flags.append(fl)
-                ties.append(nt)
+    for p in pooled_maps(q, k, block_q, block_k, scale, softmax=True):
+        for row in p:
+            kept, fl, nt = nabla_select_row(row, thr)
+            m = np.zeros(nbk, dtype=bool)
+            m[kept] = True
+            keeps.append(m)
+            flags.append(fl)
+            ties.append(nt)
     rp, ci = csr_from_bool(np.array(keeps))
     return rp, ci, np.array(flags), np.array(ties)
+
+
+def nabla_cut_admissible(p, kept, thr, tol=1e-5):
+    """Whether `kept` (block indices) is a cut that rounding of the running sums could
+    give for probabilities p at threshold thr: its mass reaches thr - tol, dropping its
+    smallest block leaves less than thr + tol (minimal), and it is a descending prefix up
+    to ties (no dropped block is more probable than a kept one by more than tol
+    relative).  For a row whose running sum at the cut lies within tol of thr (a flagged
+    row) both neighbouring cuts pass; far from the threshold only the exact cut does."""
+    p = np.asarray(p, np.float64)
+    kept = np.asarray(kept, np.int64)
+    if thr >= 1.0:
+        return len(kept) == len(p)
+    if len(kept) == 0 or len(np.unique(kept)) != len(kept):
+        return False
+    inside = np.zeros(len(p), bool)
+    inside[kept] = True
+    mass, smallest = p[inside].sum(), p[inside].min()
+    if mass < thr - tol or mass - smallest >= thr + tol:
+        return False
+    return bool(inside.all() or smallest >= p[~inside].max() * (1.0 - tol))
 
 
 # ---------------------------------------------------------- autoregressive chunk mask
@@ -279,21 +309,42 @@ def mask_ar(q, k, block_q, block_k, scale, topk, forced):
 
     Returns (row_ptr, col_idx, near_tie bool[rows]); near_tie marks rows whose k-th
     and (k+1)-th selected logits differ by less than 1e-5 relative."""
-    B, _, Hh, _ = q.shape
     nbk = -(-k.shape[1] // block_k)
+    is_forced = forced_flags(forced, nbk)
+    keeps, ties = [], []
+    for z in pooled_maps(q, k, block_q, block_k, scale, softmax=False):
+        for row in z:
+            kept, tie = ar_select_row(row, topk, is_forced)
+            m = np.zeros(nbk, dtype=bool)
+            m[kept] = True
+            keeps.append(m)
+            ties.append(tie)
+    rp, ci = csr_from_bool(np.array(keeps))
+    return rp, ci, np.array(ties)
+
+
+def forced_flags(forced, nbk):
+    """bool [nbk]: the key blocks inside the forced [lo, hi) ranges."""
     is_forced = np.zeros(nbk, dtype=bool)
     for lo, hi in forced:
         is_forced[lo:hi] = True
-    keeps, ties = [], []
-    for b in range(B):
-        for h in range(Hh):
-            z = _pooled_logits(np.asarray(q[b, :, h, :], np.float64),
-                               np.asarray(k[b, :, h, :], np.float64), block_q, block_k, scale)
-            for row in z:
-                kept, tie = ar_select_row(row, topk, is_forced)
-                m = np.zeros(nbk, dtype=bool)
-                m[kept] = True
-                keeps.append(m)
-                ties.append(tie)
-    rp, ci = csr_from_bool(np.array(keeps))
-    return rp, ci, np.array(ties)
+    return is_forced
+
+
+def topk_admissible(z, kept, topk, is_forced, tol=1e-5):
+    """Whether `kept` is a selection that rounding of the logits could give: every forced
+    block, exactly `topk` others, and no unselected candidate's logit above a selected
+    one's by more than tol relative (the k-th / (k+1)-th tie window of mask_ar)."""
+    z = np.asarray(z, np.float64)
+    kept = np.asarray(kept, np.int64)
+    inside = np.zeros(len(z), bool)
+    inside[kept] = True
+    if len(np.unique(kept)) != len(kept) or not inside[is_forced].all():
+        return False
+    sel, rest = inside & ~is_forced, ~inside & ~is_forced
+    if sel.sum() != min(topk, (~is_forced).sum()):
+        return False
+    if not rest.any() or not sel.any():
+        return True
+    lo, hi = z[sel].min(), z[rest].max()
+    return bool(hi - lo <= tol * max(abs(lo), 1e-300))

@@ -140,6 +140,11 @@ def test_attn_validation(L):
     assert attn(L, scale=-0.1)[0] == E_PARAM
     assert attn(L, o=ODD)[0] == E_UNSUP
     assert attn(L, query=True) == (OK, 0)
+    # bf16 token rows of 2^24 bytes or more: the kernels' 24-bit row offsets would wrap
+    assert attn(L, H=65536, D=128)[0] == E_UNSUP
+    assert attn(L, H=65536, D=128, query=True)[0] == E_UNSUP
+    assert attn(L, H=65535, D=128, query=True)[0] == OK
+    assert attn(L, H=65536, D=128, dtype=0, query=True)[0] == OK      # fp32 path: no such limit
 
 
 def tiled(L, q=FAKE, dtype=1, B=1, H=2, D=128, grid=(12, 16, 16), tile=(6, 8, 8), rp=FAKE, ci=FAKE, slabs=1,
@@ -252,9 +257,9 @@ def test_kv_validation(L):
     assert L.vsa_mask_remap(FAKE, FAKE, 1, 0, FAKE, 16, FAKE, NULL) == E_SHAPE
 
 
-def bwd(L, q=FAKE, dtype=1, D=128, slabs=1, scale=0.1, ws=FAKE, nbytes=10 ** 9, dq=FAKE, query=False):
+def bwd(L, q=FAKE, dtype=1, H=2, D=128, slabs=1, scale=0.1, ws=FAKE, nbytes=10 ** 9, dq=FAKE, query=False):
     nb = ctypes.c_size_t(nbytes)
-    st = L.vsa_block_sparse_attn_bwd(q, FAKE, FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE, dtype, 1, 2, D, 100, 90,
+    st = L.vsa_block_sparse_attn_bwd(q, FAKE, FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE, dtype, 1, H, D, 100, 90,
                                      64, 64, FAKE, FAKE, slabs, scale, NULL if query else ws, ctypes.byref(nb), NULL)
     return st, nb.value
 
@@ -273,3 +278,5 @@ def test_bwd_validation(L):
     assert bwd(L, nbytes=need - 1)[0] == E_CAP
     assert bwd(L, dq=NULL)[0] == E_NULL
     assert bwd(L, dq=ODD)[0] == E_UNSUP
+    assert bwd(L, H=65536, query=True)[0] == E_UNSUP                 # bf16 rows of 2^24 bytes
+    assert bwd(L, H=65535, query=True)[0] == OK

@@ -382,3 +382,61 @@ def test_sta_heads_per_head_counts_and_order():
     s = 2
     lo = rp[s * n]
     assert np.array_equal(ci[lo:lo + n], np.arange(n))
+
+
+# --------------------------------------------- admissible answers for flagged rows
+def test_nabla_cut_admissible():
+    """The exact cut is always admissible; one block more or fewer, or a kept block swapped
+    for a less probable one, is not, unless the running sum at the cut lies within 1e-5 of
+    the threshold (then both neighbouring cuts are)."""
+    rng = np.random.default_rng(21)
+    for _ in range(200):
+        n = int(rng.integers(2, 40))
+        p = _random_row(rng, n)
+        thr = float(rng.uniform(0.05, 0.99))
+        kept, flagged, _ = oracle.nabla_select_row(p, thr)
+        assert oracle.nabla_cut_admissible(p, kept, thr)
+        order = np.argsort(-p, kind="stable")
+        k = len(kept)
+        if flagged:
+            continue
+        assert not oracle.nabla_cut_admissible(p, order[:k - 1], thr) or k == 1
+        if k < n:
+            assert not oracle.nabla_cut_admissible(p, order[:k + 1], thr)
+            gap = p[order[k - 1]] - p[order[k]]
+            if gap > 1e-5 * p[order[k - 1]]:            # not a tie: the swap is a different answer
+                swapped = np.concatenate([order[:k - 1], order[k:k + 1]])
+                assert not oracle.nabla_cut_admissible(p, swapped, thr)
+    # running sums exactly on the threshold: both cuts are admissible, a third is not
+    p = np.array([0.5, 0.25, 0.125, 0.125])
+    assert oracle.nabla_cut_admissible(p, [0, 1], 0.75)
+    assert oracle.nabla_cut_admissible(p, [0, 1, 2], 0.75)
+    assert not oracle.nabla_cut_admissible(p, [0, 1, 2, 3], 0.75)
+    assert not oracle.nabla_cut_admissible(p, [0, 2], 0.6)            # not a prefix
+    assert not oracle.nabla_cut_admissible(p, [], 0.6)
+    assert oracle.nabla_cut_admissible(p, [0, 1, 2, 3], 1.0)
+    assert not oracle.nabla_cut_admissible(p, [0, 1, 2], 1.0)
+
+
+def test_topk_admissible():
+    z = np.array([3.0, 1.0, 4.0, 1.0, 5.0, 9.0, 2.0, 6.0])
+    forced = oracle.forced_flags([(0, 1), (7, 8)], len(z))
+    kept, _ = oracle.ar_select_row(z, 3, forced)
+    assert list(kept) == [0, 2, 4, 5, 7]
+    assert oracle.topk_admissible(z, kept, 3, forced)
+    assert not oracle.topk_admissible(z, [0, 2, 4, 5], 3, forced)          # a forced block missing
+    assert not oracle.topk_admissible(z, [0, 1, 4, 5, 7], 3, forced)       # 1.0 chosen over 4.0
+    assert not oracle.topk_admissible(z, [0, 2, 4, 5, 6, 7], 3, forced)    # one too many
+    # the 3rd and 4th candidates tie within 1e-5: either one is admissible
+    z2 = z.copy()
+    z2[6] = 4.0 * (1 - 1e-7)
+    assert oracle.topk_admissible(z2, [0, 4, 5, 6, 7], 3, forced)
+    assert oracle.topk_admissible(z2, [0, 2, 4, 5, 7], 3, forced)
+    rng = np.random.default_rng(22)
+    for _ in range(100):
+        n = int(rng.integers(5, 60))
+        zr = rng.standard_normal(n)
+        fr = rng.random(n) < 0.2
+        kk = int(rng.integers(1, 5))
+        kept, _ = oracle.ar_select_row(zr, kk, fr)
+        assert oracle.topk_admissible(zr, kept, kk, fr)
