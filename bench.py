@@ -7,11 +7,11 @@ the GPU with the inputs resident in HBM:
 For the STA workloads (sta, sta_heads) the reorder is folded into the attention
 kernel's row addresses (vsa_tiled_attn_fwd on raster-order tokens): the step is
 the mask, then that call; --unfused runs the separate passes instead.
-The default workload is the STA one (24 heads, head_dim 128, bf16, 30x48x80 =
-115,200 tokens, 6x8x8 tiles = 384-token blocks on a 5x6x10 tile grid, 3x3x5 tile
-window clipped at the border); --workload nabla | radial | ar | nabla_sta |
-sta_heads | ar_compact measures the others (their lines are reports, not the
-headline).
+The default workload is the radial one, the largest (24 heads, head_dim 128, bf16,
+125x45x80 = 450,000 tokens, 3,600 per frame, raster 128-token blocks, radial
+energy-decay mask; the attention runs as vsa_radial_attn_fwd, query blocks at the
+same place of consecutive frames grouped); --workload sta | nabla | ar | nabla_sta | sta_heads |
+ar_compact measures the others (their lines are reports, not the headline).
 
 value       = kept-block attention FLOPs (4 * D * sum of nq*nk over kept block
               pairs, true token counts) / wall time of a step, TFLOP/s.
@@ -19,13 +19,17 @@ roofline    = the attention kernel alone: the same FLOPs / its mean launch time
               measured with HIP events on its stream, against the bf16 dense
               MFMA peak (2.5 PFLOP/s).
 speedup     = the same kernel on an all-ones mask (dense attention) / sparse.
-cpu_baseline= the fp64 oracle on a bounded sample (the same path for a subset of
-              heads), FLOPs counted the same way (STA workload only).
+cpu_baseline= the fp64 oracle on the same path: its mask in full, its attention on
+              sampled query blocks, extrapolated linearly in kept pairs to the
+              whole path (FLOPs counted the same way); it also compares the
+              oracle's mask with the GPU's, row by row.
+hbm_passes  = SICS scores, the NABLA block mean-pool and (tiled workloads) the tile
+              reorder, each timed alone with the caches flushed before every rep.
 sclk        = the GFX clock (amdsmi, mean over the XCDs) while the attention kernel
               runs back to back for --clock-s seconds after the timed steps; the
               roofline's frac_at_measured_sclk scales the peak by it / 2.4 GHz.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sta]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload radial]
                        [--no-dense] [--no-cpu] [--no-bwd] [--unfused] [--clock-s S]
 """
 import argparse
@@ -80,13 +84,16 @@ def attn_flops(rp, ci, block_q, block_k, nq, nk, D, bh, n_slabs):
     return 4.0 * D * total * (bh if n_slabs == 1 else 1)
 
 
-def attn_kernel_name(D, block_q, block_k, grouped=False, batch=1, heads=1, n_qblocks=1, tiled=False):
-    """Label of the bf16 instantiation the library launches.  Query blocks of <= 128 rows
-    are grouped (when the library asks for a workspace) into 12-, 8- or 4-wave
-    workgroups, the first width whose group count keeps enough workgroups; otherwise it
-    picks a 4-wave key split (<= 64 rows) or 12-, 8- or 4-wave workgroups from block_q.  The
-    fifth flag: raster-order tokens with the tiles as blocks (the fused tile reorder); the
-    last number: stream tiles per LDS stage (two for grouped, untiled key blocks of <= 64)."""
+def attn_kernel_name(D, block_q, block_k, grouped=False, batch=1, heads=1, n_qblocks=1, tiled=False,
+                     n_kblocks=0):
+    """Label of the bf16 instantiation the library launches (its plan, mirrored here).  With a
+    workspace (grouped=True), query blocks of <= 128 rows are grouped into 12-, 8- or 4-wave
+    workgroups, the first width whose group count keeps enough workgroups; otherwise it picks
+    a 4-wave key split (<= 64 rows) or 12-, 8- or 4-wave workgroups from block_q, and, with a
+    workspace, splits each row's key stream into chunks when the rows cannot fill one round
+    of workgroups.  Template arguments: head_dim, key split, waves, grouped, tiled
+    (raster-order tokens with the tiles as blocks), stream tiles per LDS stage (two for
+    grouped, untiled key blocks of <= 64), split key streams."""
     tl = str(tiled).lower()
     if grouped:
         wpb = -(-block_q // 32)
@@ -96,10 +103,14 @@ def attn_kernel_name(D, block_q, block_k, grouped=False, batch=1, heads=1, n_qbl
                 continue
             if batch * heads * -(-n_qblocks // G) >= (512 if nw == 4 else 256):
                 tw = 2 if nw >= 8 and block_k <= 64 and not tiled else 1
-                return f"attn_fwd_bf16_kernel<{D}, 1, {nw}, true, {tl}, {tw}>"
+                return f"attn_fwd_bf16_kernel<{D}, 1, {nw}, true, {tl}, {tw}, false>"
     ks = 2 if block_q <= 64 else 1
     nw = 4 if ks == 2 else (12 if block_q % 384 == 0 else (8 if block_q % 256 == 0 else 4))
-    return f"attn_fwd_bf16_kernel<{D}, {ks}, {nw}, false, {tl}, 1>"
+    items = batch * heads * n_qblocks * -(-block_q // (32 * nw // ks))
+    slots = 256 * (2 if nw == 4 else 1)
+    n = min(-(-4 * slots // items), 8, n_kblocks // 8)
+    sp = grouped and items < slots and n_kblocks >= 16 and n >= 2
+    return f"attn_fwd_bf16_kernel<{D}, {ks}, {nw}, false, {tl}, 1, {str(sp).lower()}>"
 
 
 def source_hash(path):
@@ -184,34 +195,151 @@ class ClockSampler:
                           f"{self.interval_s * 1e3:.0f} ms while {what}; second half of the samples"}
 
 
-def cpu_baseline(x, cfg, target_s=12.0):
-    """The fp64 oracle on a bounded sample: the same path (reorder, STA mask,
-    attention, inverse reorder) for whole heads, taken in order until about
-    target_s seconds of CPU work have run."""
+def _oracle_mask(name, cfg, qt, kt):
+    """The oracle's mask of a workload: (row_ptr, col_idx, flagged rows or None).  qt, kt:
+    fp64 [B, N, heads, D] in the attention order (only the NABLA and top-k masks read them)."""
+    import oracle
+    D = cfg["head_dim"]
+    if name == "sta":
+        return (*oracle.mask_sta(cfg["grid"], cfg["tile"], cfg["window"]), None)
+    if name == "sta_heads":
+        wins = [cfg["windows"][h % len(cfg["windows"])] for h in range(cfg["heads"])]
+        return (*oracle.mask_sta_heads(cfg["grid"], cfg["tile"], wins, cfg["batch"]), None)
+    if name == "radial":
+        T, Hg, Wg = cfg["grid"]
+        return (*oracle.mask_radial(T, Hg * Wg, cfg["block"]), None)
+    if name in ("nabla", "nabla_sta"):
+        bq = cfg["tile"][0] * cfg["tile"][1] * cfg["tile"][2]
+        rp, ci, fl, _ = oracle.mask_nabla(qt, kt, bq, bq, D ** -0.5, cfg["threshold"])
+        if name == "nabla_sta":
+            nbq = len(rp) // (cfg["batch"] * cfg["heads"])
+            rps, cis = oracle.mask_sta(cfg["grid"], cfg["tile"], cfg["window"])
+            rp, ci = oracle.mask_union(rp, ci, cfg["batch"] * cfg["heads"], rps, cis, 1, nbq)
+        return rp, ci, fl
+    T, Hg, Wg = cfg["grid"]
+    forced = oracle.ar_forced_ranges(Hg * Wg, T, cfg["anchor_frames"], cfg["recent_frames"], cfg["block"])
+    rp, ci, ties = oracle.mask_ar(qt, kt, cfg["block"], cfg["block"], D ** -0.5, cfg["topk"], forced)
+    return rp, ci, ties
+
+
+def _mask_rows_differ(rp_a, ci_a, rp_b, ci_b):
+    """bool per row: the two CSR masks keep different blocks."""
+    la, lb = np.diff(rp_a), np.diff(rp_b)
+    out = la != lb
+    for r in np.nonzero(~out)[0]:
+        out[r] = not np.array_equal(ci_a[rp_a[r]:rp_a[r + 1]], ci_b[rp_b[r]:rp_b[r + 1]])
+    return out
+
+
+def cpu_baseline(name, cfg, x, path, rp_gpu, ci_gpu, flops_total, target_s=15.0):
+    """The fp64 oracle on the same path, on a bounded sample.
+
+    The mask is computed in full (the tile reorder of Q and K it needs included); the
+    attention runs on runs of 16 consecutive query blocks, head by head in a seeded order,
+    each head's Q, K, V converted to fp64 and tile-reordered, and the output rows reordered
+    back, until about target_s seconds have run (every block at the small autoregressive
+    shape).  The full path's time is extrapolated: t_mask + t_setup * heads / heads seen +
+    t_runs * (all kept pairs / sampled pairs), and the rate is the path's kept-block FLOPs
+    over that time.
+    As a by-product the oracle's mask is compared row by row with the GPU's."""
     import oracle
     from threadpoolctl import threadpool_info
-    grid, tile, window = cfg["grid"], cfg["tile"], cfg["window"]
-    D = cfg["head_dim"]
-    bq = tile[0] * tile[1] * tile[2]
-    N = x["q"].shape[1]
+    B, H, D = cfg["batch"], cfg["heads"], cfg["head_dim"]
+    scale = D ** -0.5
+    bq, bk = path.bq, path.bk
+    nq, nk = path.nq, path.nk
+    perm = oracle.tile_order_source(cfg["grid"], cfg["tile"]) if path.tiled else None
+    dyn = name in ("nabla", "nabla_sta", "ar", "ar_compact")
+    # mask stage (timed): reorder of Q and K for the dynamic masks, then the mask
     t0 = time.perf_counter()
-    rp, ci = oracle.mask_sta(grid, tile, window)
-    flops, heads_done = 0.0, 0
-    for h in range(cfg["heads"]):
-        qh, kh, vh = (x[w][:, :, h:h + 1].double().numpy() for w in ("q", "k", "v"))
-        qt, kt, vt = (oracle.tile_reorder(a, grid, tile) for a in (qh, kh, vh))
-        o, _ = oracle.attention(qt, kt, vt, rp, ci, bq, bq, D ** -0.5, 1)
-        oracle.tile_reorder(o, grid, tile, inverse=True)
-        flops += attn_flops(rp, ci, bq, bq, N, N, D, 1, 1)
-        heads_done += 1
-        if time.perf_counter() - t0 > target_s:
+    qt = kt = None
+    if dyn:
+        qt, kt = (x[w].double().numpy() for w in ("q", "k"))
+        if perm is not None:
+            qt, kt = qt[:, perm], kt[:, perm]
+    rp, ci, flags = _oracle_mask(name, cfg, qt, kt)
+    t_mask = time.perf_counter() - t0
+    del qt, kt
+    check = {"rows": int(len(rp) - 1), "rows_differ": None}
+    if len(rp) == len(rp_gpu):
+        diff = _mask_rows_differ(rp, ci, rp_gpu, ci_gpu)
+        check["rows_differ"] = int(diff.sum())
+        if flags is not None:
+            check.update(flagged=int(flags.sum()), flagged_differ=int((diff & flags).sum()),
+                         unflagged_differ=int((diff & ~flags).sum()))
+    # attention on sampled runs of 16 consecutive query blocks (timed), per head, with the
+    # oracle's own mask.  A head's setup (its Q, K, V to fp64 and into the attention order) is
+    # timed apart and extrapolated by heads; the runs are extrapolated by kept pairs.
+    nbq = -(-nq // bq)
+    n_slabs = path.n_slabs
+    rng = np.random.default_rng(np.random.SeedSequence([cfg["seed"], 98]))
+    ksz = np.minimum(bk, nk - np.arange(-(-nk // bk)) * bk)
+    qsz = np.minimum(bq, nq - np.arange(nbq) * bq)
+    t_setup, t_attn, pairs_done, blocks_done, heads_seen = 0.0, 0.0, 0, 0, 0
+    full = name in ("ar", "ar_compact")
+    run = 16
+    for h in rng.permutation(H):
+        b = 0
+        base = 0 if n_slabs == 1 else (b * H + h) * nbq
+        t1 = time.perf_counter()
+        qh, kh, vh = (x[w][b, :, h].double().numpy() for w in ("q", "k", "v"))
+        if perm is not None:
+            qh, kh, vh = qh[perm], kh[perm], vh[perm]
+        t_setup += time.perf_counter() - t1
+        heads_seen += 1
+        starts = np.arange(0, nbq, run)
+        for c0 in (starts if full else rng.permutation(starts)):
+            c1 = min(nbq, c0 + run)
+            sub_rp = (rp[base + c0:base + c1 + 1] - rp[base + c0]).astype(np.int64)
+            sub_ci = ci[rp[base + c0]:rp[base + c1]]
+            q0, q1 = c0 * bq, min(nq, c1 * bq)
+            t1 = time.perf_counter()
+            o, _ = oracle.attention(qh[None, q0:q1, None], kh[None, :, None], vh[None, :, None], sub_rp, sub_ci,
+                                    bq, bk, scale, 1)
+            if perm is not None:                                       # the output rows back to raster order
+                o_r = np.empty((q1 - q0, D))
+                o_r[np.argsort(perm[q0:q1])] = o[0, :, 0]
+            t_attn += time.perf_counter() - t1
+            for i in range(c0, c1):
+                pairs_done += int(qsz[i]) * int(ksz[ci[rp[base + i]:rp[base + i + 1]]].sum())
+            blocks_done += c1 - c0
+            if not full and t_attn + t_setup > target_s:
+                break
+        if not full and t_attn + t_setup > target_s:
             break
-    dt = time.perf_counter() - t0
+    pairs_total = flops_total / (4.0 * D)
+    t_est = t_mask + t_setup * B * H / heads_seen + t_attn * pairs_total / max(pairs_done, 1)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 numpy oracle, full path (reorder, STA mask, attention, inverse reorder) for "
-                      f"{heads_done} of {cfg['heads']} heads, {dt:.1f} s wall; host has "
-                      f"{len(os.sched_getaffinity(0))} cores available"}
+    extrapolated = pairs_done < pairs_total
+    return {"value": flops_total / t_est / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "extrapolated": bool(extrapolated), "t_mask_s": round(t_mask, 3), "t_head_setup_s": round(t_setup, 3),
+            "t_attn_sample_s": round(t_attn, 3),
+            "t_path_s": round(t_est, 3), "mask_check": check,
+            "sample": (f"fp64 numpy oracle: the full mask ({'with the tile reorder of Q and K it reads, ' if dyn and perm is not None else ''}"
+                       f"{t_mask:.1f} s), then attention on {blocks_done} of {B * H * nbq} (head, query block) "
+                       f"pairs in runs of {run} from {heads_seen} heads ({t_attn:.1f} s, output rows reordered back; "
+                       f"{t_setup:.1f} s for the heads' inputs to fp64{' and tile order' if perm is not None else ''}), "
+                       + ("extrapolated to the whole path (runs by kept key-query pairs, setup by heads); "
+                          if extrapolated else "")
+                       + f"host has {len(os.sched_getaffinity(0))} cores available")}
+
+
+def time_hbm_pass(fn, stream, flush, reps=10):
+    """Median and minimum of `reps` HIP-event timings of fn on `stream`, each after reading
+    the flush buffer (written once; larger than the 256 MB Infinity Cache and the L2s), so
+    that every rep reads its input from HBM.  A read leaves clean lines behind: writing the
+    buffer before each rep would leave dirty lines that drain during the timed call."""
+    fn()
+    ms = []
+    for _ in range(reps):
+        flush.amax()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        ms.append(a.elapsed_time(b))
+    return float(np.median(ms)), float(np.min(ms))
 
 
 class Path:
@@ -289,9 +417,16 @@ class Path:
                                                        workspace=ws, row_ptr=self.rp, col_idx=self.ci,
                                                        **sel)
         self.ci = torch.empty(cap, dtype=torch.int32, device=dev)
+        # radial: query blocks at the same place of consecutive frames share a workgroup
+        # (vsa_radial_attn_fwd); the other untiled workloads group consecutive blocks
+        self.frame_tokens = cfg["grid"][1] * cfg["grid"][2] if name == "radial" else None
         # workspace of the forward (union lists when small query blocks run grouped), sized
         # once: the step allocates nothing
-        nws = vsa.attn_fwd_workspace_bytes(self.qa, self.ka, self.rp, self.ci, self.bq, self.bk, self.n_slabs)
+        if self.frame_tokens:
+            nws = vsa.attn_fwd_workspace_bytes_radial(self.qa, self.ka, self.rp, self.ci, self.bq, self.frame_tokens,
+                                                      self.n_slabs)
+        else:
+            nws = vsa.attn_fwd_workspace_bytes(self.qa, self.ka, self.rp, self.ci, self.bq, self.bk, self.n_slabs)
         if self.fused:
             nws = max(nws, vsa.tiled_attn_workspace_bytes(self.q, *self.tiled, self.rp, self.ci, self.n_slabs))
         self.ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
@@ -347,7 +482,8 @@ class Path:
         self.vsa.vsa_block_sparse_attn_fwd(self.qa, self.ka, self.va, self.rp if rp is None else rp,
                                            self.ci if ci is None else ci, self.bq, self.bk,
                                            self.n_slabs if rp is None else 1, self.scale,
-                                           out=self.oa, lse=self.lse, workspace=wsx, grouped=wsx is not None)
+                                           out=self.oa, lse=self.lse, workspace=wsx, grouped=wsx is not None,
+                                           frame_tokens=self.frame_tokens)
 
     def reorder_out(self):
         if self.tiled:
@@ -359,7 +495,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="sta", choices=sorted(DESCRIPTION))
+    ap.add_argument("--workload", default="radial", choices=sorted(DESCRIPTION))
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -440,6 +576,8 @@ def main():
     if not args.no_dense:
         drp, dci = path.vsa.all_ones_mask(path.nbq, path.nbk, dev)
         nwd = (path.vsa.tiled_attn_workspace_bytes(path.q, *path.tiled, drp, dci, 1) if path.fused else
+               path.vsa.attn_fwd_workspace_bytes_radial(path.qa, path.ka, drp, dci, path.bq, path.frame_tokens, 1)
+               if path.frame_tokens else
                path.vsa.attn_fwd_workspace_bytes(path.qa, path.ka, drp, dci, path.bq, path.bk, 1))
         dws = torch.empty(nwd, dtype=torch.uint8, device=dev) if nwd else None
         path.attn(drp, dci, dws)
@@ -486,27 +624,39 @@ def main():
         print(f"[bench] backward {bwd_ms:.3f} ms ({bwd['tflops']:.1f} TFLOP/s at 2.5x forward FLOPs)",
               file=sys.stderr, flush=True)
 
-    # SICS block scores (SPADE's scheme-step score) of the attention-order K, timed on their
-    # own, outside the step: HBM-bound, reported against the HBM peak and as a fraction of
-    # the attention time.
+    # HBM-bound passes, each timed on its own outside the step with the caches flushed
+    # before every rep (median and minimum of the reps), against the HBM peak:
+    #   SICS block scores (SPADE's scheme-step score) of the attention-order K;
+    #   the block mean-pool of the NABLA mask (its first pass), over the same K;
+    #   the tile reorder of one token tensor, where the path has tiles.
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)     # 1 GiB
+    k_bytes = path.ka.numel() * path.ka.element_size()
+
+    def hbm(ms_med, ms_min, nbytes, **extra):
+        gbs = nbytes / (ms_med * 1e-3) / 1e9
+        return {"ms_median": round(ms_med, 4), "ms_min": round(ms_min, 4), "bytes": nbytes, "gbs": round(gbs, 1),
+                "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                "frac_hbm_at_min": round(nbytes / (ms_min * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), **extra}
+
     sics_out = torch.empty((path.B, path.H, path.nbk), dtype=torch.float64, device=dev)
-    path.vsa.vsa_block_sics(path.ka, path.bk, out=sics_out)
-    sms = []
-    for _ in range(5):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        path.vsa.vsa_block_sics(path.ka, path.bk, out=sics_out)
-        b.record(stream)
-        b.synchronize()
-        sms.append(a.elapsed_time(b))
-    sics_ms = float(np.mean(sms))
-    sics_bytes = path.ka.numel() * path.ka.element_size()
-    sics = {"ms": round(sics_ms, 4), "gbs": round(sics_bytes / (sics_ms * 1e-3) / 1e9, 1),
-            "frac_hbm": round(sics_bytes / (sics_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "ratio_to_attn": round(sics_ms / attn_ms, 5), "bytes": sics_bytes,
-            "kernel": "sics_kernel", "tensor": "K in attention order", "block": path.bk}
-    print(f"[bench] SICS of K: {sics_ms:.3f} ms, {sics['gbs']:.0f} GB/s ({100 * sics['frac_hbm']:.1f}% of HBM), "
-          f"{100 * sics['ratio_to_attn']:.2f}% of attention", file=sys.stderr, flush=True)
+    med, mn = time_hbm_pass(lambda: path.vsa.vsa_block_sics(path.ka, path.bk, out=sics_out), stream, flush)
+    sics = hbm(med, mn, k_bytes, kernel="sics_kernel", tensor="K in attention order", block=path.bk,
+               ratio_to_attn=round(med / attn_ms, 5))
+    pool_out = torch.empty((path.B, path.H, path.nbk, path.D), dtype=torch.float64, device=dev)
+    med, mn = time_hbm_pass(lambda: path.vsa.vsa_block_mean_pool(path.ka, path.bk, out=pool_out), stream, flush)
+    pool = hbm(med, mn, k_bytes, kernel="pool_kernel<true>", tensor="K in attention order", block=path.bk,
+               bytes_written=pool_out.numel() * 8,
+               gbs_with_writes=round((k_bytes + pool_out.numel() * 8) / (med * 1e-3) / 1e9, 1))
+    reorder = None
+    if path.tiled:
+        med, mn = time_hbm_pass(lambda: path.vsa.vsa_tile_reorder(path.k, *path.tiled, out=path.ka), stream, flush)
+        reorder = hbm(med, mn, 2 * k_bytes, kernel="tile_reorder_kernel", tensor="K, raster -> tile-major")
+    del flush
+    for nm, r in (("SICS", sics), ("pool", pool), ("reorder", reorder)):
+        if r is not None:
+            print(f"[bench] {nm}: median {r['ms_median']:.3f} ms (min {r['ms_min']:.3f}), {r['gbs']:.0f} GB/s "
+                  f"({100 * r['frac_hbm']:.1f}% of HBM; {100 * r['frac_hbm_at_min']:.1f}% at the minimum)",
+                  file=sys.stderr, flush=True)
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE.format(name)):
@@ -516,9 +666,10 @@ def main():
             traffic = tr.get("bytes_per_launch")
 
     cpu = None
-    if name == "sta" and not args.no_cpu:
-        cpu = cpu_baseline(x, cfg)
-        print(f"[bench] cpu baseline {cpu['value']:.4f} TFLOP/s ({cpu['sample']})", file=sys.stderr, flush=True)
+    if not args.no_cpu:
+        cpu = cpu_baseline(name, cfg, x, path, rp_h, ci_h, flops)
+        print(f"[bench] cpu baseline {cpu['value']:.4f} TFLOP/s ({cpu['sample']}); mask check {cpu['mask_check']}",
+              file=sys.stderr, flush=True)
 
     token_bytes = path.q.numel() * path.q.element_size()
     reorder_ms = (float(np.mean(ev["reorder_in"]) + np.mean(ev["reorder_out"])) if "reorder_in" in ev else None)
@@ -542,8 +693,8 @@ def main():
                    "parallelism": "none (one GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": attn_kernel_name(path.D, path.bq, path.bk, path.ws is not None, path.B, path.H, path.nbq,
-                                                                 path.fused),
+                     "traffic": traffic, "kernel": attn_kernel_name(path.D, path.bq, path.bk, path.ws is not None,
+                                                                 path.B, path.H, path.nbq, path.fused, path.nbk),
                      "flops_per_launch": flops, "ms_per_launch": round(attn_ms, 4),
                      # the same fraction against the peak scaled to the mean clock sampled in
                      # the timed steps (the published peak assumes 2.4 GHz)
@@ -557,7 +708,9 @@ def main():
         "dense_ms": None if dense is None else round(dense["ms"], 3),
         "dense_tflops": None if dense is None else round(dense["tflops"], 2),
         "stage_ms": {k_: round(float(np.mean(v_)), 4) for k_, v_ in ev.items()},
-        "sics": sics,
+        "hbm_passes": {"sics": sics, "pool": pool, "tile_reorder": reorder,
+                       "method": "HIP events around each call, the caches flushed (a 1 GiB buffer read) before "
+                                 "each of 10 reps; GB/s from the median"},
         "backward": bwd,
         "kv_compaction": (None if path.compact is None else
                           {"tokens_before": path.nk, "tokens_after": path.n_out,
@@ -565,8 +718,8 @@ def main():
                            "ms": round(float(np.mean(ev["compact"])), 4),
                            "bytes_moved": 2 * 2 * path.B * path.n_out * path.H * path.D * path.k.element_size()}),
         "mask_over_attn": round(float(np.mean(ev["mask"])) / attn_ms, 5),
-        "reorder_gbs": (round(4 * 2 * token_bytes / (reorder_ms * 1e-3) / 1e9, 1)
-                        if path.tiled and reorder_ms else None),
+        "reorder_in_step_gbs": (round(4 * 2 * token_bytes / (reorder_ms * 1e-3) / 1e9, 1)
+                                if path.tiled and reorder_ms else None),
         "tile_reorder": (None if not path.tiled else
                          "folded into the attention kernel (raster-order q, k, v, o)" if path.fused else
                          "separate passes: q, k, v in, o out"),

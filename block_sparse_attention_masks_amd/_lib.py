@@ -38,6 +38,7 @@ _SIGS = {
     "vsa_mask_sta_heads": ([_I32] * 6 + [_P, _I32, _I64, _P, _P, _I64, _P], _I32),
     "vsa_mask_union": ([_I64, _I32, _P, _P, _I64, _P, _P, _I64, _P, _P, _I64, _P], _I32),
     "vsa_block_sics": ([_P, _I32, _I64, _I32, _I32, _I64, _I32, _P, _P], _I32),
+    "vsa_block_mean_pool": ([_P, _I32, _I64, _I32, _I32, _I64, _I32, _P, _P], _I32),
     "vsa_block_sparse_attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I64, _I64, _I32,
                                    _I32, _P, _P, _I32, _F32, _P, ctypes.POINTER(ctypes.c_size_t), _P], _I32),
     "vsa_kv_plan": ([_P, _P, _I64, _I64, _I64, _I32, _P, _P, _P], _I32),
@@ -47,6 +48,8 @@ _SIGS = {
                         ctypes.POINTER(Select), _P, _P, _I64, _P, ctypes.POINTER(ctypes.c_size_t), _P], _I32),
     "vsa_block_sparse_attn_fwd": ([_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I64, _I64, _I32, _I32,
                                    _P, _P, _I32, _F32, _P, ctypes.POINTER(ctypes.c_size_t), _P], _I32),
+    "vsa_radial_attn_fwd": ([_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I64, _I64, _I32, _I32, _I64,
+                             _P, _P, _I32, _F32, _P, ctypes.POINTER(ctypes.c_size_t), _P], _I32),
     "vsa_tiled_attn_fwd": ([_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                             _P, _P, _I32, _F32, _P, ctypes.POINTER(ctypes.c_size_t), _P], _I32),
 }
@@ -201,6 +204,24 @@ def vsa_mask_union(rp_a, ci_a, slabs_a, rp_b, ci_b, slabs_b, n_qblocks, n_kblock
                                 slabs_b, _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), _stream(row_ptr)),
            "vsa_mask_union")
     return row_ptr, col_idx
+
+
+def vsa_block_mean_pool(x, block, out=None):
+    """Mean of each block's valid token rows of x [B, N, heads, head_dim] (bf16 or fp32)
+    -> fp64 [B, heads, ceil(N / block), head_dim]."""
+    _require(x, "x")
+    if x.dtype not in _DTYPE:
+        raise ValueError("x must be bfloat16 or float32")
+    B, N, H, D = x.shape
+    nb = -(-N // block)
+    if out is None:
+        out = torch.empty((B, H, nb, D), dtype=torch.float64, device=x.device)
+    _require(out, "out", x.device)
+    if out.dtype != torch.float64 or tuple(out.shape) != (B, H, nb, D):
+        raise ValueError("out must be float64 [B, heads, n_blocks, head_dim]")
+    _check(lib().vsa_block_mean_pool(_ptr(x), _DTYPE[x.dtype], B, H, D, N, block, _ptr(out), _stream(x)),
+           "vsa_block_mean_pool")
+    return out
 
 
 def vsa_block_sics(x, block, out=None):
@@ -386,14 +407,35 @@ def vsa_mask_nabla(q, k, block_q, block_k, scale=None, threshold=None, topk=0, f
     return row_ptr, col_idx
 
 
+def vsa_radial_attn_fwd(q, k, v, row_ptr, col_idx, block, frame_tokens, n_slabs=1, scale=None, out=None, lse=None,
+                        want_lse=True, workspace=None, grouped=True):
+    """vsa_block_sparse_attn_fwd for masks over raster-order frames of frame_tokens tokens:
+    with a workspace, query blocks at the same place of consecutive frames share a
+    workgroup (same result; only the work order differs)."""
+    return vsa_block_sparse_attn_fwd(q, k, v, row_ptr, col_idx, block, block, n_slabs, scale, out, lse, want_lse,
+                                     workspace, grouped, frame_tokens=frame_tokens)
+
+
+def attn_fwd_workspace_bytes_radial(q, k, row_ptr, col_idx, block, frame_tokens, n_slabs=1):
+    """Workspace bytes of vsa_radial_attn_fwd (0: none)."""
+    B, nq, Hh, D = q.shape
+    nb = ctypes.c_size_t(0)
+    _check(lib().vsa_radial_attn_fwd(_ptr(q), _ptr(k), _ptr(k), _ptr(q), None, _DTYPE[q.dtype], B, Hh, D, nq,
+                                     k.shape[1], block, block, frame_tokens, _ptr(row_ptr), _ptr(col_idx), n_slabs,
+                                     1.0, None, ctypes.byref(nb), None), "vsa_radial_attn_fwd")
+    return nb.value
+
+
 def vsa_block_sparse_attn_fwd(q, k, v, row_ptr, col_idx, block_q, block_k, n_slabs=1, scale=None,
-                              out=None, lse=None, want_lse=True, workspace=None, grouped=True):
+                              out=None, lse=None, want_lse=True, workspace=None, grouped=True, frame_tokens=None):
     """Exact softmax attention over the kept blocks -> (o, lse or None).
 
-    Small query blocks run grouped (several blocks per workgroup over the union of their
-    kept blocks) when a workspace is available: it is allocated here unless given, and
-    grouped=False runs without one (same results; bit for bit for blocks of 65 to 128 rows,
-    to rounding for blocks of at most 64 rows, whose ungrouped run splits each key tile)."""
+    With a workspace (allocated here unless given), small query blocks run grouped
+    (several blocks per workgroup over the union of their kept blocks), and problems with
+    too few rows to fill the chip split each row's key stream over several workgroups and
+    merge the parts.  grouped=False runs without a workspace: neither grouped nor split
+    (same results; bit for bit for grouped blocks of 65 to 128 rows, to rounding
+    otherwise)."""
     for name, t in (("q", q), ("k", k), ("v", v), ("row_ptr", row_ptr), ("col_idx", col_idx)):
         _require(t, name, q.device)
     B, nq, Hh, D = q.shape
@@ -409,13 +451,16 @@ def vsa_block_sparse_attn_fwd(q, k, v, row_ptr, col_idx, block_q, block_k, n_sla
     _require(out, "out", q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hh, nq), dtype=torch.float32, device=q.device)
-    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _DTYPE[q.dtype], B, Hh, D, nq, nk, block_q, block_k,
-            _ptr(row_ptr), _ptr(col_idx), n_slabs, float(scale))
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _DTYPE[q.dtype], B, Hh, D, nq, nk, block_q, block_k)
+    tail = (_ptr(row_ptr), _ptr(col_idx), n_slabs, float(scale))
+    if frame_tokens is None:
+        name, fn, args = "vsa_block_sparse_attn_fwd", lib().vsa_block_sparse_attn_fwd, head + tail
+    else:
+        name, fn, args = "vsa_radial_attn_fwd", lib().vsa_radial_attn_fwd, head + (int(frame_tokens),) + tail
     nb = ctypes.c_size_t(0)
     if grouped:
         if workspace is None:
-            _check(lib().vsa_block_sparse_attn_fwd(*args, None, ctypes.byref(nb), _stream(q)),
-                   "vsa_block_sparse_attn_fwd")
+            _check(fn(*args, None, ctypes.byref(nb), _stream(q)), name)
             if nb.value:
                 workspace = torch.empty(nb.value, dtype=torch.uint8, device=q.device)
         if workspace is not None:
@@ -423,9 +468,8 @@ def vsa_block_sparse_attn_fwd(q, k, v, row_ptr, col_idx, block_q, block_k, n_sla
             nb = ctypes.c_size_t(workspace.numel())
     else:
         workspace = None
-    _check(lib().vsa_block_sparse_attn_fwd(*args, _ptr(workspace) if workspace is not None else None,
-                                           ctypes.byref(nb) if workspace is not None else None, _stream(q)),
-           "vsa_block_sparse_attn_fwd")
+    _check(fn(*args, _ptr(workspace) if workspace is not None else None,
+              ctypes.byref(nb) if workspace is not None else None, _stream(q)), name)
     return out, lse
 
 

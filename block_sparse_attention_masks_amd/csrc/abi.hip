@@ -150,7 +150,8 @@ vsa_status vsa_block_sics(const void* x, int32_t dtype, int64_t batch, int32_t h
   const vsa_status st = check_tokens(dtype, batch, heads, head_dim, n, n, block, block);
   if (st != VSA_OK) return st;
   if (!aligned16(x)) return VSA_ERR_UNSUPPORTED;
-  if (ceil_div(n, block) > 0x7fffffff / 2 || batch > 65535) return VSA_ERR_SHAPE;
+  if (ceil_div(n, block) * ceil_div((int64_t)heads * head_dim, 512) > kI32Max || batch > 65535)
+    return VSA_ERR_SHAPE;
   return from_hip(vsa::launch_block_sics(x, dtype == VSA_BF16, batch, heads, head_dim, n, block, scores,
                                          stream));
 }
@@ -191,6 +192,17 @@ vsa_status vsa_mask_remap(const int32_t* row_ptr, const int32_t* col_idx, int64_
                                          n_slabs, col_out, stream));
 }
 
+vsa_status vsa_block_mean_pool(const void* x, int32_t dtype, int64_t batch, int32_t heads, int32_t head_dim,
+                               int64_t n, int32_t block, double* out, hipStream_t stream) {
+  if (!x || !out) return VSA_ERR_NULL;
+  const vsa_status st = check_tokens(dtype, batch, heads, head_dim, n, n, block, block);
+  if (st != VSA_OK) return st;
+  if (batch > 65535 || ceil_div(n, block) * ceil_div((int64_t)heads * head_dim, 512) > kI32Max)
+    return VSA_ERR_SHAPE;
+  if (!aligned16(x) || ((uintptr_t)out & 7u)) return VSA_ERR_UNSUPPORTED;
+  return from_hip(vsa::launch_block_pool(x, dtype == VSA_BF16, batch, heads, head_dim, n, block, out, stream));
+}
+
 vsa_status vsa_mask_nabla(const void* q, const void* k, int32_t dtype, int64_t batch,
                           int32_t heads, int32_t head_dim, int64_t nq, int64_t nk,
                           int32_t block_q, int32_t block_k, double scale, const vsa_select* sel,
@@ -200,6 +212,7 @@ vsa_status vsa_mask_nabla(const void* q, const void* k, int32_t dtype, int64_t b
   vsa_status st = check_tokens(dtype, batch, heads, head_dim, nq, nk, block_q, block_k);
   if (st != VSA_OK) return st;
   const int64_t nbq = ceil_div(nq, block_q), nbk = ceil_div(nk, block_k);
+  if (batch > 65535 || (nbq + nbk) * ceil_div((int64_t)heads * head_dim, 512) > kI32Max) return VSA_ERR_SHAPE;
   if (nbk > 4096) return VSA_ERR_UNSUPPORTED;
   if (!(scale == scale)) return VSA_ERR_PARAM;
   if (sel->topk < 0 || sel->n_forced < 0 || sel->n_forced > 16) return VSA_ERR_PARAM;
@@ -230,13 +243,16 @@ vsa_status vsa_mask_nabla(const void* q, const void* k, int32_t dtype, int64_t b
   return from_hip(vsa::launch_mask_nabla(a, stream));
 }
 
-vsa_status vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o,
-                                     float* lse, int32_t dtype, int64_t batch, int32_t heads,
-                                     int32_t head_dim, int64_t nq, int64_t nk, int32_t block_q,
-                                     int32_t block_k, const int32_t* row_ptr,
-                                     const int32_t* col_idx, int32_t n_slabs, float scale,
-                                     void* workspace, size_t* workspace_bytes,
-                                     hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward on untiled tokens, with query blocks grouped `group_stride` blocks apart.
+vsa_status attn_fwd_untiled(const void* q, const void* k, const void* v, void* o, float* lse, int32_t dtype,
+                            int64_t batch, int32_t heads, int32_t head_dim, int64_t nq, int64_t nk,
+                            int32_t block_q, int32_t block_k, const int32_t* row_ptr, const int32_t* col_idx,
+                            int32_t n_slabs, float scale, int group_stride, void* workspace,
+                            size_t* workspace_bytes, hipStream_t stream) {
   if (!q || !k || !v || !o || !row_ptr || !col_idx) return VSA_ERR_NULL;
   vsa_status st = check_tokens(dtype, batch, heads, head_dim, nq, nk, block_q, block_k);
   if (st != VSA_OK) return st;
@@ -245,6 +261,7 @@ vsa_status vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v
   if (dtype == VSA_BF16 && !bf16_rows_fit(heads, head_dim)) return VSA_ERR_UNSUPPORTED;
   vsa::AttnArgs a{q, k, v, o, lse, dtype, batch, heads, head_dim, nq, nk, block_q, block_k,
                   row_ptr, col_idx, n_slabs, scale};
+  a.group_stride = group_stride;
   const size_t want = dtype == VSA_BF16 ? vsa::attn_fwd_workspace(a) : 0;
   if (workspace_bytes && !workspace) {  // size query
     *workspace_bytes = want;
@@ -254,6 +271,33 @@ vsa_status vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v
   if (workspace && ((uintptr_t)workspace & 255u)) return VSA_ERR_UNSUPPORTED;
   const size_t have = workspace && workspace_bytes ? *workspace_bytes : 0;
   return from_hip(vsa::launch_attn_fwd(a, workspace, have, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+vsa_status vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                                     float* lse, int32_t dtype, int64_t batch, int32_t heads,
+                                     int32_t head_dim, int64_t nq, int64_t nk, int32_t block_q,
+                                     int32_t block_k, const int32_t* row_ptr,
+                                     const int32_t* col_idx, int32_t n_slabs, float scale,
+                                     void* workspace, size_t* workspace_bytes,
+                                     hipStream_t stream) {
+  return attn_fwd_untiled(q, k, v, o, lse, dtype, batch, heads, head_dim, nq, nk, block_q, block_k, row_ptr,
+                          col_idx, n_slabs, scale, 1, workspace, workspace_bytes, stream);
+}
+
+vsa_status vsa_radial_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t dtype,
+                               int64_t batch, int32_t heads, int32_t head_dim, int64_t nq, int64_t nk,
+                               int32_t block_q, int32_t block_k, int64_t frame_tokens, const int32_t* row_ptr,
+                               const int32_t* col_idx, int32_t n_slabs, float scale, void* workspace,
+                               size_t* workspace_bytes, hipStream_t stream) {
+  if (frame_tokens <= 0 || block_q <= 0) return VSA_ERR_SHAPE;
+  const int64_t stride = std::max<int64_t>(1, frame_tokens / block_q);
+  if (stride > kI32Max / 16) return VSA_ERR_SHAPE;
+  return attn_fwd_untiled(q, k, v, o, lse, dtype, batch, heads, head_dim, nq, nk, block_q, block_k, row_ptr,
+                          col_idx, n_slabs, scale, (int)stride, workspace, workspace_bytes, stream);
 }
 
 vsa_status vsa_tiled_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

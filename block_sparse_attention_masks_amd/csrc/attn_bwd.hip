@@ -191,8 +191,11 @@ struct Work {
 // slab share a 4-wave workgroup (wpb waves each) and walk the union of the query blocks
 // that keep any of them; list u = slab * n_groups + group holds cnt[u] entries at
 // idx[u * cap ..], each with a mask of the group's key blocks that it keeps.
+// The lists are kernel arguments of their own (idx in row_idx's place, mask, cnt), declared
+// __restrict__ like the CSC view, so that the compiler reads them with scalar loads: through
+// a struct's pointers they were vector loads whose waits also waited for the copies just
+// issued.
 struct KeyGroups {
-  const int32_t *idx, *mask, *cnt;
   int G, wpb, cap;
 };
 
@@ -538,7 +541,8 @@ __global__ __launch_bounds__(kNW * kWave, 2) void dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     float* __restrict__ dk, float* __restrict__ dv, int64_t nq, int64_t nk, int heads, int block_q, int block_k,
-    const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ row_idx, int n_slabs, float scale,
+    const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ row_idx,
+    const int32_t* __restrict__ gmask, const int32_t* __restrict__ gcnt, int n_slabs, float scale,
     float scale_log2, Work wk, KeyGroups gp) {
   static_assert(!GR || KS == 1, "grouped key blocks use whole query tiles");
   __shared__ __attribute__((aligned(1024))) Smem<D> sm;
@@ -580,7 +584,7 @@ __global__ __launch_bounds__(kNW * kWave, 2) void dkdv_kernel(
   Tiles it;
   if constexpr (GR) {
     const int64_t u = slab * wk.nb + kb;
-    it = Tiles{gp.idx, (int)(u * gp.cap), (int)(u * gp.cap) + gp.cnt[u], 0, 0, block_q, (int)nq};
+    it = Tiles{row_idx, (int)(u * gp.cap), (int)(u * gp.cap) + gcnt[u], 0, 0, block_q, (int)nq};
   } else {
     const int64_t c = slab * wk.nb + kb;
     it = Tiles{row_idx, col_ptr[c], col_ptr[c + 1], 0, 0, block_q, (int)nq};
@@ -645,17 +649,23 @@ __global__ __launch_bounds__(kNW * kWave, 2) void dkdv_kernel(
   int buf = 0;
   while (it.valid()) {
     if (nx.valid()) {
+      // the next tile's lse and D first: a wait for these loads then leaves the copies issued
+      // after them in flight (loads complete in order)
+      if (w == 0) fetch_ld(nx.r0, nx.re, lv, dv_);
       CopyPlan<D>::issue_lean(qbase, dobase, nx.r0, nx.re, row_bytes, row_stride, sm.a[buf ^ 1], sm.b[buf ^ 1], w,
                               lane());
-      if (w == 0) fetch_ld(nx.r0, nx.re, lv, dv_);
     }
     const uint16_t* sq = sm.a[buf];
     const uint16_t* sd = sm.b[buf];
-    const bool member = !GR || ((gp.mask[it.e] >> lk) & 1);
+    const bool member = !GR || ((gmask[it.e] >> lk) & 1);
 #pragma unroll
     for (int qs = 0; qs < NQS; ++qs) {
       if (!member) break;
       const int q32 = 32 * (qh + qs);  // first query of this 32-query step within the tile
+      // the fragment rows and lane halves from an opaque lane id, remade at each step: kept
+      // live across the loop, their 16 read offsets were spilled, and the reload's wait
+      // also waited for the copies of the next tile
+      const int ln = lane(), rq = q32 + (ln & 31), gq = ln >> 5;
       // S, then P (fp32, kept in s) and its bf16 copy, then dV^T += dO^T P; rows past the
       // tile's end have lse = +inf, so P = 0 there
       f32x16 s;
@@ -663,7 +673,7 @@ __global__ __launch_bounds__(kNW * kWave, 2) void dkdv_kernel(
       for (int a = 0; a < 16; ++a) s[a] = 0.f;
 #pragma unroll
       for (int kd = 0; kd < D / 16; ++kd)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(sq, q32 + col, kd, g), kf[kd], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(sq, rq, kd, gq), kf[kd], s, 0, 0, 0);
       bf16x8 pb[2];
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
@@ -691,7 +701,7 @@ __global__ __launch_bounds__(kNW * kWave, 2) void dkdv_kernel(
       for (int a = 0; a < 16; ++a) dp[a] = 0.f;
 #pragma unroll
       for (int kd = 0; kd < D / 16; ++kd)
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(sd, q32 + col, kd, g), vf[kd], dp, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(sd, rq, kd, gq), vf[kd], dp, 0, 0, 0);
       bf16x8 db[2];
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
@@ -902,13 +912,15 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, void* workspace, hipStream_t st
   int32_t* row_idx = (int32_t*)ws;
   ws += al(4 * (size_t)(a.n_slabs * nbq * nbk));
   const KeyGroupPlan kg = plan_key_groups(a);
-  KeyGroups kgp{nullptr, nullptr, nullptr, 1, 1, 0};
+  KeyGroups kgp{1, 1, 0};
+  int32_t *gidx = nullptr, *gmask = nullptr, *gcnt = nullptr;
   if (kg.G) {
-    int32_t* gidx = (int32_t*)ws;
+    gidx = (int32_t*)ws;
     ws += al(4 * (size_t)(kg.lists * nbq));
-    int32_t* gmask = (int32_t*)ws;
+    gmask = (int32_t*)ws;
     ws += al(4 * (size_t)(kg.lists * nbq));
-    kgp = KeyGroups{gidx, gmask, (int32_t*)ws, kg.G, kg.wpb, nbq};
+    gcnt = (int32_t*)ws;
+    kgp = KeyGroups{kg.G, kg.wpb, nbq};
   }
 
   const bool bf16 = a.dtype == 1;
@@ -949,8 +961,8 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, void* workspace, hipStream_t st
   Work wkv = make_work(a.batch, a.heads, a.nk, a.block_k, 32 * kNW / ksk);
   if (kg.G) {  // the union of each group's query blocks, from the CSC view
     hipLaunchKernelGGL(group_union_kernel, dim3((unsigned)((kg.lists + kUnionWaves - 1) / kUnionWaves)),
-                       dim3(kUnionWaves * kWave), 0, stream, col_ptr, row_idx, nbk, kg.lists, kg.G, kg.n_groups,
-                       nbq, (int32_t*)kgp.idx, (int32_t*)kgp.mask, (int32_t*)kgp.cnt);
+                       dim3(kUnionWaves * kWave), 0, stream, col_ptr, row_idx, nbk, kg.lists, kg.G, kg.n_groups, 1,
+                       nbq, gidx, gmask, gcnt);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     wkv.nb = kg.n_groups;
     wkv.mt_per_b = 1;
@@ -966,8 +978,8 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, void* workspace, hipStream_t st
   auto lk = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3((unsigned)(wkv.per_xcd * 8)), dim3(kNW * kWave), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
-                       a.lse, delta, a.dk, a.dv, a.nq, a.nk, a.heads, a.block_q, a.block_k, col_ptr, row_idx,
-                       a.n_slabs, a.scale, sl2, wkv, kgp);
+                       a.lse, delta, a.dk, a.dv, a.nq, a.nk, a.heads, a.block_q, a.block_k, col_ptr,
+                       kg.G ? gidx : row_idx, gmask, gcnt, a.n_slabs, a.scale, sl2, wkv, kgp);
   };
   if (a.head_dim == 64) {
     ksq == 2 ? lq(dq_kernel<64, 2>) : lq(dq_kernel<64, 1>);

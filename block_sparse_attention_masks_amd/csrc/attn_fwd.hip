@@ -42,6 +42,7 @@
 // one thread per query row (used for small fp32 problems).
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "group_union.h"
@@ -69,10 +70,26 @@ struct Work {
 
 // Grouped query blocks: G consecutive query blocks of a slab share a workgroup of G * wpb
 // waves and walk the union of their kept key blocks.  List u = slab * n_groups + group
-// holds cnt[u] entries at col[u * cap ..], each with a mask of the rows that keep it.
+// holds cnt[u] entries at col[u * cap ..], each with a mask of the rows that keep it.  The
+// lists themselves are kernel arguments of their own (col in col_idx's place, mask, cnt),
+// declared __restrict__ like the CSR: that is what lets the compiler read them with scalar
+// loads.  Read through a struct's pointers they became vector loads, and the wait for such
+// a load also waited for the next tile's copies just issued, so no copy overlapped compute.
 struct Groups {
-  const int32_t *col, *mask, *cnt;
   int G, wpb, cap;
+  int stride;  // group c stride + j holds query blocks c stride G + j + i stride, i < G
+};
+
+// Split key streams (SP): a row's kept-block list is cut into n contiguous chunks, each
+// walked by its own workgroup, when there are too few rows to fill the chip.  A chunk
+// writes its unnormalised fp32 output and (reference maximum in log2 units, row sum) for
+// each of its rows (tiled: indexed by the raster row, the order of o and lse);
+// split_merge_kernel adds the chunks in a fixed order.
+struct Split {
+  float* o;      // [n][rows][D]
+  float* ml;     // [n][rows][2]
+  int64_t rows;  // batch * heads * nq
+  int n;
 };
 
 // Tokens in raster order of a T x H x W grid cut into tt x th x tw tiles, the attention
@@ -274,13 +291,14 @@ struct Smem {
   uint16_t v[2 * TW][kBN * D];
 };
 
-template <int D, int KS, int NW, bool GR, bool TL, int TW>
+template <int D, int KS, int NW, bool GR, bool TL, int TW, bool SP>
 __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
     int64_t nq, int64_t nk, int heads, int block_q, int block_k,
-    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int n_slabs,
-    float scale_log2, Work wk, Groups gp, Tiling tg) {
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+    const int32_t* __restrict__ gmask, const int32_t* __restrict__ gcnt, int n_slabs,
+    float scale_log2, Work wk, Groups gp, Tiling tg, Split sp) {
   __shared__ __attribute__((aligned(1024))) Smem<D, TW> sm;
   // TW = 2: two stream tiles per stage, so per wait and barrier.  That pays off for grouped
   // blocks of 64 rows, where consecutive tiles belong to different key blocks and so often
@@ -299,8 +317,13 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
   // work item: (batch, head, query block, row tile) -- or, grouped, (batch, head, group
   // of gp.G query blocks); wk.nbq counts query blocks or groups
   const int64_t bid = blockIdx.x;
-  const int64_t item = (bid % 8) * wk.per_xcd + bid / 8;
+  int64_t item = (bid % 8) * wk.per_xcd + bid / 8;
   if (item >= wk.items) return;
+  int chunk = 0;  // SP: the chunk of the row's key stream, innermost
+  if constexpr (SP) {
+    chunk = (int)(item % sp.n);
+    item /= sp.n;
+  }
   const int mt = (int)(item % wk.mt_per_qb);
   int64_t rest = item / wk.mt_per_qb;
   const int qb = (int)(rest % wk.nbq);
@@ -319,7 +342,7 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
   int lq = 0;  // grouped: the wave's query block within the group
   if constexpr (GR) {
     lq = w / gp.wpb;
-    const int64_t qbw = (int64_t)qb * gp.G + lq;
+    const int64_t qbw = (int64_t)(qb / gp.stride) * gp.stride * gp.G + qb % gp.stride + (int64_t)lq * gp.stride;
     q_w = qbw * block_q + (int64_t)(w % gp.wpb) * 32;
     q_hi = lq < gp.G ? min(min((qbw + 1) * block_q, nq), q_w + 32) : q_w;
   } else {
@@ -333,10 +356,15 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
   TileIter it;
   if constexpr (GR) {  // the union of the group's kept blocks, with a row-membership mask
     const int64_t u = slab * wk.nbq + qb;
-    it = TileIter{gp.col, (int)(u * gp.cap), (int)(u * gp.cap) + gp.cnt[u], 0, 0, block_k, (int)nk};
+    it = TileIter{col_idx, (int)(u * gp.cap), (int)(u * gp.cap) + gcnt[u], 0, 0, block_k, (int)nk};
   } else {
     const int64_t r = slab * wk.nbq + qb;
     it = TileIter{col_idx, row_ptr[r], row_ptr[r + 1], 0, 0, block_k, (int)nk};
+  }
+  if constexpr (SP) {  // this chunk's share of the entries, split as evenly as integers allow
+    const int e0 = it.e, ne = it.e1 - it.e;
+    it.e = e0 + (int)((int64_t)ne * chunk / sp.n);
+    it.e1 = e0 + (int)((int64_t)ne * (chunk + 1) / sp.n);
   }
   if constexpr (TL) it.open(tg);
   else it.open();
@@ -466,7 +494,7 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
     const uint16_t* sk = sm.k[buf];
     const uint16_t* sv = sm.v[buf];
     // grouped: a wave whose query block does not keep this key block only helps copy it
-    if (!GR || ((gp.mask[it.e] >> lq) & 1)) {
+    if (!GR || ((gmask[it.e] >> lq) & 1)) {
     f32x16 s[NST];
 #pragma unroll
     for (int st = 0; st < NST; ++st)
@@ -587,6 +615,25 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
     m_ref = mm;
   }
   const float l_tot = l_run + xchg32(l_run, g);
+  if constexpr (SP) {  // the chunk's unnormalised output, its reference maximum and row sum
+    if (my_q < q_hi) {
+      const int64_t row = (int64_t)chunk * sp.rows + (b * heads + h) * nq + my_row;  // tiled: raster row
+      float* op = sp.o + row * D;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          float4 ov;
+          ov.x = acc_o[t][4 * a4];
+          ov.y = acc_o[t][4 * a4 + 1];
+          ov.z = acc_o[t][4 * a4 + 2];
+          ov.w = acc_o[t][4 * a4 + 3];
+          *(float4*)(op + 32 * t + 8 * a4 + 4 * g) = ov;
+        }
+      if (g == 0) *(float2*)(sp.ml + 2 * row) = float2{m_ref, l_tot};
+    }
+    return;
+  }
   if (my_q < q_hi) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* op = o + ((b * nq + my_row) * heads + h) * D;
@@ -604,6 +651,44 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
       lse[(b * heads + h) * nq + my_row] =
           l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f : -INFINITY;
   }
+}
+
+// Merge of split key streams: thread = 4 output elements of one (batch, head, query) row.
+// With m the largest of the chunks' reference maxima, chunk c counts with weight
+// 2^(m_c - m); the chunks are added in order c = 0, 1, ..., so the result is deterministic.
+template <int D>
+__global__ __launch_bounds__(256) void split_merge_kernel(const float* __restrict__ opart,
+                                                          const float* __restrict__ ml, int n, int64_t rows,
+                                                          int heads, int64_t nq, uint16_t* __restrict__ o,
+                                                          float* __restrict__ lse) {
+  constexpr int C = D / 4;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= rows * C) return;
+  const int64_t row = gid / C;
+  const int d0 = (int)(gid % C) * 4;
+  float m = -INFINITY;
+  for (int c = 0; c < n; ++c) m = fmaxf(m, ml[2 * (c * rows + row)]);
+  float l = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (m != -INFINITY) {
+    for (int c = 0; c < n; ++c) {
+      const float2 mc = *(const float2*)(ml + 2 * (c * rows + row));
+      const float a = __builtin_amdgcn_exp2f(mc.x - m);
+      l += a * mc.y;
+      const float4 x = *(const float4*)(opart + (c * rows + row) * D + d0);
+      acc[0] += a * x.x;
+      acc[1] += a * x.y;
+      acc[2] += a * x.z;
+      acc[3] += a * x.w;
+    }
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const int64_t q = row % nq, bh = row / nq, h = bh % heads, b = bh / heads;
+  bf16x4 ov;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(acc[i] * inv);
+  *(bf16x4*)(o + ((b * nq + q) * heads + h) * D + d0) = ov;
+  if (lse != nullptr && d0 == 0)
+    lse[row] = l > 0.f ? (m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f : -INFINITY;
 }
 
 // fp32: one thread per (batch, head, query); plain online softmax over the kept keys.
@@ -665,8 +750,48 @@ struct FwdPlan {
   bool grouped;
   int ks, nw, G, wpb, n_groups;
   size_t ws_bytes;
-  int tw = 1;  // stream tiles per LDS stage
+  int tw = 1;      // stream tiles per LDS stage
+  int splits = 1;  // chunks per row's key stream (split_merge_kernel adds them)
 };
+
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workgroups the chip runs at once for a given width (one 8- or 12-wave workgroup per CU,
+// or two 4-wave ones: the LDS stages take 64 KB each).
+constexpr int kCUs = 256;
+inline int64_t wg_slots(int nw) { return (int64_t)kCUs * (nw == 4 ? 2 : 1); }
+
+// Split each row's key stream when the rows alone cannot fill one round of workgroups on
+// the chip: enough chunks for about kSplitRounds rounds, at most 8, and on average at least
+// 8 key blocks per chunk (the kept-list lengths are only known on the device; n_kblocks
+// bounds them).  Returns the bytes of the partial outputs, n * rows * (D + 2) fp32, or 0
+// when the problem is not split.  (Between one and two rounds, splitting was measured to
+// gain nothing: 888 rows of 115 64-key tiles ran 0.473 ms unsplit and 0.475 ms in two
+// chunks; such a problem is bound by the bytes copied per flop, not by occupancy.)
+constexpr int kSplitRounds = 2;
+size_t plan_split(const AttnArgs& a, FwdPlan& p, int64_t items) {
+  const int64_t slots = wg_slots(p.nw);
+  const int64_t nbk = (a.nk + a.block_k - 1) / a.block_k;
+  p.splits = 1;
+  if (items >= slots || nbk < 16) return 0;
+  int64_t n = (kSplitRounds * slots + items - 1) / items;
+  n = std::min<int64_t>(n, std::min<int64_t>(8, nbk / 8));
+  if (n < 2) return 0;
+  const int64_t rows = a.batch * a.heads * a.nq;
+  p.splits = (int)n;
+  return align256(4 * (size_t)(n * rows * a.head_dim)) + align256(8 * (size_t)(n * rows));
+}
+
+// Groups of G query blocks `stride` apart over nbq blocks: whole runs of stride * G blocks,
+// each giving `stride` groups (the last run's groups may be partly or wholly past nbq).
+int64_t group_count(int64_t nbq, int G, int stride) {
+  return (nbq + (int64_t)stride * G - 1) / ((int64_t)stride * G) * stride;
+}
+
+// Workspace bytes of the union lists of a grouped plan: entries, row masks, counts.
+size_t union_bytes(int64_t lists, int64_t nbk) {
+  return 2 * align256(4 * (size_t)(lists * nbk)) + align256(4 * (size_t)lists);
+}
 
 FwdPlan plan_fwd(const AttnArgs& a, bool have_ws) {
   FwdPlan p{false, 1, 4, 1, 1, 0, 0};
@@ -677,13 +802,11 @@ FwdPlan plan_fwd(const AttnArgs& a, bool have_ws) {
     for (int nw : {12, 8, 4}) {
       if (nw % wpb) continue;
       const int G = nw / wpb;
-      const int64_t n_groups = (nbq + G - 1) / G;
+      const int64_t n_groups = group_count(nbq, G, a.group_stride);
       const int64_t items = a.batch * a.heads * n_groups;
       const int64_t lists = (int64_t)a.n_slabs * n_groups;
       if (G < 2 || items < (nw == 4 ? 512 : 256) || lists * nbk > 0x7fffffff) continue;
-      p = FwdPlan{true, 1, nw, G, wpb, (int)n_groups, 0};
-      auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-      p.ws_bytes = 2 * al(4 * (size_t)(lists * nbk)) + al(4 * (size_t)lists);
+      p = FwdPlan{true, 1, nw, G, wpb, (int)n_groups, union_bytes(lists, nbk)};
       break;
     }
   }
@@ -692,9 +815,13 @@ FwdPlan plan_fwd(const AttnArgs& a, bool have_ws) {
     if (p.nw >= 8 && a.block_k <= kBN && !a.tiled) p.tw = 2;
     return p;
   }
-  const bool want = p.grouped;
-  p = FwdPlan{false, a.block_q <= kBM / 2 ? 2 : 1, 4, 1, 1, 0, want ? p.ws_bytes : 0};
+  const size_t want_ws = p.grouped ? p.ws_bytes : 0;
+  p = FwdPlan{false, a.block_q <= kBM / 2 ? 2 : 1, 4, 1, 1, 0, 0};
   if (p.ks == 1) p.nw = a.block_q % 384 == 0 ? 12 : (a.block_q % 256 == 0 ? 8 : 4);
+  const int bm = 32 * p.nw / p.ks;
+  const size_t part = plan_split(a, p, a.batch * a.heads * nbq * ((a.block_q + bm - 1) / bm));
+  if (!have_ws) p.splits = 1;  // without a workspace: one workgroup per row
+  p.ws_bytes = std::max(part, want_ws);
   return p;
 }
 
@@ -779,21 +906,24 @@ hipError_t launch_attn_fwd(const AttnArgs& a, void* workspace, size_t workspace_
   const float sl2 = a.scale * kLog2e;
   const FwdPlan pl = plan_fwd(a, workspace != nullptr && workspace_bytes >= plan_fwd(a, true).ws_bytes);
   Work wk;
-  Groups gp{nullptr, nullptr, nullptr, 1, 1, 0};
+  Groups gp{1, 1, 0, 1};
+  const int32_t *kcol = a.col_idx, *gmask = nullptr, *gcnt = nullptr;
   if (pl.grouped) {
     const int nbk = (int)((a.nk + a.block_k - 1) / a.block_k);
     const int64_t lists = (int64_t)a.n_slabs * pl.n_groups;
-    auto al = [](size_t x) { return (x + 255) / 256 * 256; };
     char* ws = (char*)workspace;
     int32_t* gcol = (int32_t*)ws;
-    int32_t* gmask = (int32_t*)(ws + al(4 * (size_t)(lists * nbk)));
-    int32_t* gcnt = (int32_t*)(ws + 2 * al(4 * (size_t)(lists * nbk)));
+    int32_t* gmask_w = (int32_t*)(ws + align256(4 * (size_t)(lists * nbk)));
+    int32_t* gcnt_w = (int32_t*)(ws + 2 * align256(4 * (size_t)(lists * nbk)));
+    gmask = gmask_w;
+    gcnt = gcnt_w;
     hipLaunchKernelGGL(group_union_kernel, dim3((unsigned)((lists + kUnionWaves - 1) / kUnionWaves)),
                        dim3(kUnionWaves * kWave), 0, stream, a.row_ptr, a.col_idx, nbq, lists, pl.G, pl.n_groups,
-                       nbk, gcol, gmask, gcnt);
+                       a.group_stride, nbk, gcol, gmask_w, gcnt_w);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    gp = Groups{gcol, gmask, gcnt, pl.G, pl.wpb, nbk};
+    gp = Groups{pl.G, pl.wpb, nbk, a.group_stride};
+    kcol = gcol;
     wk.nbq = pl.n_groups;
     wk.mt_per_qb = 1;
   } else {
@@ -801,13 +931,20 @@ hipError_t launch_attn_fwd(const AttnArgs& a, void* workspace, size_t workspace_
     wk.nbq = nbq;
     wk.mt_per_qb = (a.block_q + bm - 1) / bm;
   }
-  wk.items = a.batch * a.heads * (int64_t)wk.nbq * wk.mt_per_qb;
+  Split sp{nullptr, nullptr, a.batch * a.heads * a.nq, pl.splits};
+  if (pl.splits > 1) {  // the partial outputs, after the union lists of a grouped plan
+    char* base = (char*)workspace +
+                 (pl.grouped ? union_bytes((int64_t)a.n_slabs * pl.n_groups, (a.nk + a.block_k - 1) / a.block_k) : 0);
+    sp.o = (float*)base;
+    sp.ml = (float*)(base + align256(4 * (size_t)(pl.splits * sp.rows * a.head_dim)));
+  }
+  wk.items = a.batch * a.heads * (int64_t)wk.nbq * wk.mt_per_qb * pl.splits;
   wk.per_xcd = (wk.items + 7) / 8;
   const dim3 grid((unsigned)(wk.per_xcd * 8));
   auto launch = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(pl.nw * kWave), 0, stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.nq, a.nk,
-                       a.heads, a.block_q, a.block_k, a.row_ptr, a.col_idx, a.n_slabs, sl2, wk, gp, tg);
+                       a.heads, a.block_q, a.block_k, a.row_ptr, kcol, gmask, gcnt, a.n_slabs, sl2, wk, gp, tg, sp);
   };
   // instantiation for (head_dim, plan, tiled)
   auto pick = [&](auto dc, auto tc) {
@@ -815,16 +952,25 @@ hipError_t launch_attn_fwd(const AttnArgs& a, void* workspace, size_t workspace_
     constexpr bool TL = decltype(tc)::value;
     if (pl.grouped) {
       if constexpr (!TL) {
-        if (pl.tw == 2 && pl.nw == 12) return launch(attn_fwd_bf16_kernel<D, 1, 12, true, false, 2>);
-        if (pl.tw == 2) return launch(attn_fwd_bf16_kernel<D, 1, 8, true, false, 2>);
+        if (pl.tw == 2 && pl.nw == 12) return launch(attn_fwd_bf16_kernel<D, 1, 12, true, false, 2, false>);
+        if (pl.tw == 2) return launch(attn_fwd_bf16_kernel<D, 1, 8, true, false, 2, false>);
       }
-      if (pl.nw == 12) launch(attn_fwd_bf16_kernel<D, 1, 12, true, TL, 1>);
-      else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<D, 1, 8, true, TL, 1>);
-      else launch(attn_fwd_bf16_kernel<D, 1, 4, true, TL, 1>);
-    } else if (pl.ks == 2) launch(attn_fwd_bf16_kernel<D, 2, 4, false, TL, 1>);
-    else if (pl.nw == 12) launch(attn_fwd_bf16_kernel<D, 1, 12, false, TL, 1>);
-    else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<D, 1, 8, false, TL, 1>);
-    else launch(attn_fwd_bf16_kernel<D, 1, 4, false, TL, 1>);
+      if (pl.nw == 12) launch(attn_fwd_bf16_kernel<D, 1, 12, true, TL, 1, false>);
+      else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<D, 1, 8, true, TL, 1, false>);
+      else launch(attn_fwd_bf16_kernel<D, 1, 4, true, TL, 1, false>);
+      return;
+    }
+    if (pl.splits > 1) {
+      if (pl.ks == 2) launch(attn_fwd_bf16_kernel<D, 2, 4, false, TL, 1, true>);
+      else if (pl.nw == 12) launch(attn_fwd_bf16_kernel<D, 1, 12, false, TL, 1, true>);
+      else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<D, 1, 8, false, TL, 1, true>);
+      else launch(attn_fwd_bf16_kernel<D, 1, 4, false, TL, 1, true>);
+      return;
+    }
+    if (pl.ks == 2) launch(attn_fwd_bf16_kernel<D, 2, 4, false, TL, 1, false>);
+    else if (pl.nw == 12) launch(attn_fwd_bf16_kernel<D, 1, 12, false, TL, 1, false>);
+    else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<D, 1, 8, false, TL, 1, false>);
+    else launch(attn_fwd_bf16_kernel<D, 1, 4, false, TL, 1, false>);
   };
   using D64 = std::integral_constant<int, 64>;
   using D128 = std::integral_constant<int, 128>;
@@ -836,6 +982,14 @@ hipError_t launch_attn_fwd(const AttnArgs& a, void* workspace, size_t workspace_
   } else {
     if (a.tiled) pick(D128{}, Yes{});
     else pick(D128{}, No{});
+  }
+  if (pl.splits > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t threads = sp.rows * (a.head_dim / 4);
+    hipLaunchKernelGGL(a.head_dim == 64 ? split_merge_kernel<64> : split_merge_kernel<128>,
+                       dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, sp.o, sp.ml, sp.n, sp.rows,
+                       a.heads, a.nq, (uint16_t*)a.o, a.lse);
   }
   return hipGetLastError();
 }

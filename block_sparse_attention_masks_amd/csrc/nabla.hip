@@ -6,8 +6,9 @@
 // Four passes, all in fp64 so that the decision matches a plain fp64 evaluation
 // except where the cumulative mass sits within rounding of the threshold:
 //   1. pool      -- per block, exact fp64 sums of the (bf16 or fp32) token rows,
-//                   one division by the number of valid tokens.  HBM-bound: one
-//                   workgroup streams a block's rows with 16-byte loads.
+//                   one division by the number of valid tokens.  HBM-bound: the
+//                   waves of a workgroup stream parts of a block's rows with 16-byte
+//                   loads and add their parts in LDS.
 //   2. score     -- Z = Qp Kp^T * scale per (batch, head), 64x64 fp64 tiles.
 //   3. select    -- one workgroup per row: softmax of Z (NABLA) or raw Z (top-k),
 //                   bitonic sort in LDS by (value desc, block asc), fp64 running
@@ -76,20 +77,28 @@ struct Vec8 {
   }
 };
 
-// grid: x = query blocks then key blocks, y = column slices of 8*blockDim.x elements,
-// z = batch.  The host sizes blockDim.x so that the slices cover a row evenly.  Each lane
-// keeps U rows' loads in flight; the element type is a template parameter so that the
-// bf16 kernel holds only its own registers (and so keeps enough waves resident).
-constexpr int kPoolMaxThreads = 512;
+// grid: x = (block, 64-vector slice of a row) with the slice fastest (a vector = 8
+// elements; blocks are the query blocks, then the key blocks), z = batch: the workgroups
+// that run side by side read neighbouring parts of the same rows, so whole rows stream
+// from each DRAM page.  The kPoolWaves waves of a workgroup split the block's valid rows
+// into contiguous parts; lane l of every wave sums vector 64 y + l of its rows, keeping U
+// rows' loads in flight, and the parts meet in LDS.  Splitting the rows makes the waves
+// short and many (one wave per row part rather than per block), so the last round of waves
+// on the chip is a small share of the pass.  The sums of bf16 values are exact in fp64,
+// so the order in which the parts are added does not matter.  The element type is a
+// template parameter so that the bf16 kernel holds only its own registers.
+constexpr int kPoolWaves = 4;
 template <bool BF16>
-__global__ __launch_bounds__(kPoolMaxThreads) void pool_kernel(const uint8_t* __restrict__ q,
-                                                        const uint8_t* __restrict__ k,
-                                                        int64_t nq, int64_t nk, int bq, int bk,
-                                                        int nbq, int nbk, int heads, int D,
-                                                        double* __restrict__ qp,
-                                                        double* __restrict__ kp) {
-  const bool isq = (int)blockIdx.x < nbq;
-  const int blk = isq ? blockIdx.x : blockIdx.x - nbq;
+__global__ __launch_bounds__(kPoolWaves * kWave) void pool_kernel(const uint8_t* __restrict__ q,
+                                                           const uint8_t* __restrict__ k,
+                                                           int64_t nq, int64_t nk, int bq, int bk,
+                                                           int nbq, int nbk, int heads, int D, int slices,
+                                                           double* __restrict__ qp,
+                                                           double* __restrict__ kp) {
+  __shared__ double part[kPoolWaves - 1][8][kWave];
+  const int xb = blockIdx.x / slices, slice = blockIdx.x - xb * slices;
+  const bool isq = xb < nbq;
+  const int blk = isq ? xb : xb - nbq;
   const int64_t n = isq ? nq : nk;
   const int bsz = isq ? bq : bk;
   const int nb = isq ? nbq : nbk;
@@ -97,34 +106,59 @@ __global__ __launch_bounds__(kPoolMaxThreads) void pool_kernel(const uint8_t* __
   double* dst = isq ? qp : kp;
   const int64_t b = blockIdx.z;
   const int hd = heads * D;
-  const int vec = blockIdx.y * blockDim.x + threadIdx.x;  // 8-element vector index in a row
-  if (vec * 8 >= hd) return;
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  const int vec = slice * kWave + l;  // 8-element vector index in a row
+  const bool active = vec * 8 < hd;
   constexpr int esz = BF16 ? 2 : 4;
   const int64_t row_bytes = (int64_t)hd * esz;
   const int64_t t0 = (int64_t)blk * bsz, t1 = min(n, t0 + bsz);
+  const int64_t per = (t1 - t0 + kPoolWaves - 1) / kPoolWaves;
+  const int64_t r0 = min(t1, t0 + w * per), r1 = min(t1, r0 + per);
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  const uint8_t* p = src + (b * n + t0) * row_bytes + (int64_t)vec * 8 * esz;
-  int64_t t = t0;
-  constexpr int U = BF16 ? 16 : 8;
-  for (; t + U <= t1; t += U) {
-    Vec8<BF16> x[U];
+  if (active) {
+    const uint8_t* p = src + (b * n + r0) * row_bytes + (int64_t)vec * 8 * esz;
+    int64_t t = r0;
+    constexpr int U = BF16 ? 16 : 8;
+    for (; t + U <= r1; t += U) {
+      Vec8<BF16> x[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) x[u].load(p + u * row_bytes);
+      for (int u = 0; u < U; ++u) x[u].load(p + u * row_bytes);
 #pragma unroll
-    for (int u = 0; u < U; ++u) x[u].add_to(acc);
-    p += U * row_bytes;
+      for (int u = 0; u < U; ++u) x[u].add_to(acc);
+      p += U * row_bytes;
+    }
+    for (; t < r1; ++t) {
+      Vec8<BF16> x;
+      x.load(p);
+      x.add_to(acc);
+      p += row_bytes;
+    }
   }
-  for (; t < t1; ++t) {
-    Vec8<BF16> x;
-    x.load(p);
-    x.add_to(acc);
-    p += row_bytes;
+  if (w > 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part[w - 1][i][l] = acc[i];
   }
+  __syncthreads();
+  if (w > 0 || !active) return;
+#pragma unroll
+  for (int u = 0; u < kPoolWaves - 1; ++u)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += part[u][i][l];
   const double cnt = (double)(t1 - t0);
   const int e0 = vec * 8, h = e0 / D, d0 = e0 % D;   // D is a multiple of 8
   double* out = dst + (((b * heads + h) * nb) + blk) * D + d0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) out[i] = acc[i] / cnt;
+}
+
+hipError_t launch_pool(const void* q, const void* k, int bf16, int64_t batch, int heads, int D, int64_t nq,
+                       int64_t nk, int bq, int bk, int nbq, int nbk, double* qp, double* kp,
+                       hipStream_t stream) {
+  const int slices = (heads * D / 8 + kWave - 1) / kWave;
+  const dim3 grid((unsigned)((nbq + nbk) * slices), 1, (unsigned)batch);
+  hipLaunchKernelGGL(bf16 ? pool_kernel<true> : pool_kernel<false>, grid, dim3(kPoolWaves * kWave), 0, stream,
+                     (const uint8_t*)q, (const uint8_t*)k, nq, nk, bq, bk, nbq, nbk, heads, D, slices, qp, kp);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ 2. score
@@ -394,6 +428,12 @@ size_t nabla_workspace_bytes(int64_t batch, int heads, int head_dim, int64_t nq,
   return layout(batch * heads, head_dim, nbq, nbk).total;
 }
 
+hipError_t launch_block_pool(const void* x, int bf16, int64_t batch, int heads, int D, int64_t n, int block,
+                             double* out, hipStream_t stream) {
+  const int nb = (int)((n + block - 1) / block);
+  return launch_pool(x, x, bf16, batch, heads, D, n, n, block, block, nb, 0, out, out, stream);
+}
+
 hipError_t launch_mask_nabla(const NablaArgs& a, hipStream_t stream) {
   const int64_t bh = a.batch * a.heads;
   const int nbq = (int)((a.nq + a.block_q - 1) / a.block_q);
@@ -404,19 +444,8 @@ hipError_t launch_mask_nabla(const NablaArgs& a, hipStream_t stream) {
   double* kp = (double*)(ws + L.kp);
   double* z = (double*)(ws + L.z);
   uint32_t* bitmap = (uint32_t*)(ws + L.bits);
-  const int hd = a.heads * a.head_dim;
-
-  // threads per workgroup: the row's 8-element vectors split evenly into slices of at
-  // most kPoolMaxThreads, rounded up to whole waves
-  const int vpr = hd / 8;
-  const int slices = (vpr + kPoolMaxThreads - 1) / kPoolMaxThreads;
-  const int per = (vpr + slices - 1) / slices;
-  const int pool_threads = (per + kWave - 1) / kWave * kWave;
-  dim3 g1(nbq + nbk, (vpr + pool_threads - 1) / pool_threads, (unsigned)a.batch);
-  hipLaunchKernelGGL(a.dtype == 1 ? pool_kernel<true> : pool_kernel<false>, g1, dim3(pool_threads), 0,
-                     stream, (const uint8_t*)a.q, (const uint8_t*)a.k, a.nq, a.nk, a.block_q,
-                     a.block_k, nbq, nbk, a.heads, a.head_dim, qp, kp);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_pool(a.q, a.k, a.dtype == 1, a.batch, a.heads, a.head_dim, a.nq, a.nk, a.block_q,
+                            a.block_k, nbq, nbk, qp, kp, stream);
   if (e != hipSuccess) return e;
 
   dim3 g2((nbk + kTile - 1) / kTile, (nbq + kTile - 1) / kTile, (unsigned)bh);

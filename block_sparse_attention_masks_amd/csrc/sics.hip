@@ -74,19 +74,21 @@ __device__ inline double rsqrt_refined(double s) {
 constexpr int kVecs = 64;    // 8-element vectors of the row per workgroup
 constexpr int kPhases = 8;   // waves; wave p takes rows t0 + p, t0 + p + 8, ...
 
-// grid: x = blocks, y = groups of 64 vectors of the row, z = batch.  LANES = D / 8.  The
+// grid: x = (block, group of 64 vectors of the row) with the group fastest, so that the
+// workgroups that run side by side read neighbouring parts of the same rows (whole rows
+// stream from each DRAM page), z = batch.  LANES = D / 8.  The
 // element type is a template parameter, so the bf16 kernel holds only its own registers;
 // rows are loaded U at a time and widened one at a time, as they are added.
 template <int LANES, bool BF16>
 __global__ __launch_bounds__(kVecs * kPhases) void sics_kernel(const uint8_t* __restrict__ x,
                                                                int64_t n, int block, int nb, int heads, int D,
-                                                               double* __restrict__ out) {
+                                                               int groups, double* __restrict__ out) {
   __shared__ double part[kPhases - 1][kVecs][8];
-  const int blk = blockIdx.x;
+  const int blk = blockIdx.x / groups, grp = blockIdx.x - blk * groups;
   const int64_t b = blockIdx.z;
   const int hd = heads * D;
   const int l = threadIdx.x % kVecs, phase = threadIdx.x / kVecs;
-  const int vec = blockIdx.y * kVecs + l;
+  const int vec = grp * kVecs + l;
   const bool live = vec * 8 < hd;  // a head's lanes are live or dead together
   constexpr int esz = BF16 ? 2 : 4;
   const int64_t row_bytes = (int64_t)hd * esz;
@@ -156,11 +158,12 @@ hipError_t launch_block_sics(const void* x, int bf16, int64_t batch, int heads, 
                              double* scores, hipStream_t stream) {
   const int nb = (int)((n + block - 1) / block);
   const int vpr = heads * D / 8;  // 8-element vectors per row
-  const dim3 grid(nb, (vpr + kVecs - 1) / kVecs, (unsigned)batch);
+  const int groups = (vpr + kVecs - 1) / kVecs;
+  const dim3 grid((unsigned)(nb * groups), 1, (unsigned)batch);
   auto kern = D == 64 ? (bf16 ? sics_kernel<8, true> : sics_kernel<8, false>)
                       : (bf16 ? sics_kernel<16, true> : sics_kernel<16, false>);
   hipLaunchKernelGGL(kern, grid, dim3(kVecs * kPhases), 0, stream, (const uint8_t*)x, n, block, nb, heads, D,
-                     scores);
+                     groups, scores);
   return hipGetLastError();
 }
 

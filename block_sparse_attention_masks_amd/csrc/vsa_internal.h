@@ -91,6 +91,10 @@ struct NablaArgs {
 };
 size_t nabla_workspace_bytes(int64_t batch, int heads, int head_dim, int64_t nq, int64_t nk,
                              int block_q, int block_k);
+// Mean of the valid rows of each block: x [batch, n, heads, D] -> out [batch, heads, nb, D] fp64
+// (the pooling pass of the NABLA mask on one tensor).
+hipError_t launch_block_pool(const void* x, int bf16, int64_t batch, int heads, int D, int64_t n, int block,
+                             double* out, hipStream_t stream);
 hipError_t launch_mask_nabla(const NablaArgs& a, hipStream_t stream);
 
 struct AttnArgs {
@@ -112,6 +116,8 @@ struct AttnArgs {
   // tiles, in tile-major order, are the attention blocks (block_q = block_k = tt th tw)
   int tiled = 0;
   int H = 0, W = 0, tt = 0, th = 0, tw = 0;
+  // grouped query blocks: a group's blocks lie group_stride blocks apart (1: consecutive)
+  int group_stride = 1;
 };
 // How a tiled forward maps its 64-row copy tiles (0: the tile shape is not supported):
 // the tile's h-w plane must be a multiple of 64 tokens with tw dividing 64 or a multiple

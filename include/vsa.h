@@ -6,8 +6,10 @@
  * CSR list of kept key blocks (vsa_mask_sta, vsa_mask_radial, vsa_mask_nabla; composed
  * with vsa_mask_sta_heads and vsa_mask_union),
  * then compute exact softmax(Q K^T * scale) V over the kept blocks only
- * (vsa_block_sparse_attn_fwd; vsa_tiled_attn_fwd folds the reorder into it) and its
- * gradients (vsa_block_sparse_attn_bwd).
+ * (vsa_block_sparse_attn_fwd; vsa_tiled_attn_fwd folds the reorder into it;
+ * vsa_radial_attn_fwd groups its work across frames) and its gradients
+ * (vsa_block_sparse_attn_bwd).  vsa_block_mean_pool and vsa_block_sics are the
+ * pooling and scoring passes on one tensor.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -230,6 +232,25 @@ vsa_status vsa_kv_gather(const void* x, int32_t dtype, int64_t batch, int32_t he
 vsa_status vsa_mask_remap(const int32_t* row_ptr, const int32_t* col_idx, int64_t n_slabs, int64_t n_qblocks,
                           const int32_t* slot, int32_t n_kblocks, int32_t* col_out, hipStream_t stream);
 
+/*
+ * vsa_block_mean_pool -- mean of each block's token rows, per head, in fp64.
+ *
+ * NABLA explainer (aibr.jp/archives/124678), sec. 3: Q and K are average-pooled per
+ * block before the small attention map is formed.  This is that pooling step on one
+ * tensor (vsa_mask_nabla runs the same kernel on Q and K): out[b, h, i, :] = the mean
+ * over the valid tokens t of block i (the last block may be ragged) of x[b, t, h, :].
+ * The sums are accumulated in fp64 (exact for bf16 rows) and divided once by the
+ * block's token count.
+ *
+ * x     device, [batch, n, heads, head_dim], dtype VSA_BF16 or VSA_F32, 16-byte aligned.
+ * out   device, [batch, heads, ceil(n / block), head_dim] doubles, 8-byte aligned.
+ * Errors: VSA_ERR_NULL, VSA_ERR_DTYPE, VSA_ERR_SHAPE (non-positive sizes, batch above
+ * 65535, ceil(n / block) * ceil(heads * head_dim / 512) above 2^31 - 1),
+ * VSA_ERR_UNSUPPORTED (head_dim not 64/128, alignment), VSA_ERR_HIP.
+ */
+vsa_status vsa_block_mean_pool(const void* x, int32_t dtype, int64_t batch, int32_t heads, int32_t head_dim,
+                               int64_t n, int32_t block, double* out, hipStream_t stream);
+
 /* Selection rule of vsa_mask_nabla. */
 typedef struct {
   double cdf_threshold;   /* NABLA cut, in (0, 1]; used when topk == 0           */
@@ -260,7 +281,7 @@ typedef struct {
  * col_capacity must be >= batch*heads*n_qblocks*n_kblocks.
  * workspace device scratch; when workspace == NULL the call only writes the
  *           required size to *workspace_bytes and returns VSA_OK.
- * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE, VSA_ERR_DTYPE, VSA_ERR_PARAM,
+ * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE (also batch above 65535), VSA_ERR_DTYPE, VSA_ERR_PARAM,
  * VSA_ERR_CAPACITY (col_capacity or *workspace_bytes too small),
  * VSA_ERR_UNSUPPORTED (head_dim, alignment, n_kblocks > 4096), VSA_ERR_HIP.
  */
@@ -292,12 +313,18 @@ vsa_status vsa_mask_nabla(const void* q, const void* k, int32_t dtype,
  * workspace / workspace_bytes: call with workspace = NULL and workspace_bytes set
  * to get the size.  bf16 query blocks of at most 128 rows are then run grouped:
  * several consecutive query blocks share a workgroup and walk the union of their
- * kept key blocks, so one copy of a key tile serves more query rows.  The
- * workspace (device, 256-byte aligned) holds those union lists; with workspace =
- * NULL, or smaller than the query, the call runs ungrouped.  Both give the same
- * result bit for bit for query blocks of 65 to 128 rows; ungrouped blocks of at most
- * 64 rows split each key tile between two waves and add their halves at the end, so
- * there the two agree to rounding only.
+ * kept key blocks, so one copy of a key tile serves more query rows.  When the rows
+ * are too few to fill the chip once (fewer workgroups than the chip runs at a time:
+ * e.g. a few heads of short query blocks over a long key sequence), each row's
+ * kept-block list is instead cut into up to 8 contiguous chunks walked by separate workgroups, whose
+ * fp32 partial outputs (with their running maximum and row sum) a second kernel
+ * adds in chunk order: the result is deterministic and equals the unsplit run to
+ * rounding.  The workspace (device, 256-byte aligned) holds the union lists or the
+ * partial outputs; with workspace = NULL, or smaller than the query, the call runs
+ * neither grouped nor split.  Grouped and ungrouped runs give the same result bit for
+ * bit for query blocks of 65 to 128 rows; ungrouped blocks of at most 64 rows split
+ * each key tile between two waves and add their halves at the end, so there the two
+ * agree to rounding only.
  * bf16 token rows must be below 2^24 bytes (heads * head_dim * 2 < 2^24, i.e. at most
  * 65,535 heads at head_dim 128); the kernels address a tile's rows in 24-bit arithmetic.
  * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE, VSA_ERR_DTYPE, VSA_ERR_PARAM (n_slabs, scale),
@@ -313,6 +340,32 @@ vsa_status vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v
                                      int32_t n_slabs, float scale,
                                      void* workspace, size_t* workspace_bytes,
                                      hipStream_t stream);
+
+/*
+ * vsa_radial_attn_fwd -- the forward above, for masks over raster-order frames, with
+ * query blocks grouped across frames.
+ *
+ * Radial Attention explainer (aibr.jp/archives/112136), sec. 2-3: the spatial window
+ * shrinks with temporal distance, so far from its own frame a query block keeps only
+ * the key blocks around its own place in each other frame -- nearly the same key blocks
+ * as the query blocks at that place in the neighbouring frames.  With a workspace and
+ * bf16 query blocks of at most 128 rows, this call groups query blocks P apart (P =
+ * frame_tokens / block_q, rounded down, at least 1: the same place in consecutive
+ * frames) instead of consecutive ones, so the union of kept key blocks that a group
+ * walks is close to one row's.  Any CSR mask is accepted and the result is the same as
+ * vsa_block_sparse_attn_fwd's (bit for bit where both group blocks of 65 to 128 rows);
+ * only the work order differs.  The workspace size must be queried from this call.
+ *
+ * frame_tokens  tokens per frame (> 0); every other argument as for
+ *               vsa_block_sparse_attn_fwd.
+ * Errors: as for vsa_block_sparse_attn_fwd; VSA_ERR_SHAPE also for frame_tokens <= 0.
+ */
+vsa_status vsa_radial_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int32_t dtype, int64_t batch, int32_t heads, int32_t head_dim,
+                               int64_t nq, int64_t nk, int32_t block_q, int32_t block_k,
+                               int64_t frame_tokens, const int32_t* row_ptr, const int32_t* col_idx,
+                               int32_t n_slabs, float scale, void* workspace, size_t* workspace_bytes,
+                               hipStream_t stream);
 
 /*
  * vsa_tiled_attn_fwd -- the forward above on raster-order tokens of a 3D grid,
@@ -332,7 +385,8 @@ vsa_status vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v
  *             order.
  * row_ptr/col_idx  CSR over the tile-major tiles (n_tiles = T/tt * H/th * W/tw rows
  *             per slab; vsa_mask_sta's output), n_slabs = 1 or batch*heads.
- * workspace / workspace_bytes, scale: as for vsa_block_sparse_attn_fwd.
+ * workspace / workspace_bytes, scale: as for vsa_block_sparse_attn_fwd (grouping and the
+ * split of small problems included).
  * The tile's h-w plane must nest with the kernel's 64-token copy tile: th*tw a
  * multiple of 64 with tw dividing 64 or a multiple of 64, or th*tw dividing 64 (the
  * 6x8x8 and 1x8x8 tiles of the pages' video models qualify), and a tile holds at

@@ -231,6 +231,20 @@ def sics(L, x=FAKE, dtype=1, B=1, H=2, D=128, n=1000, block=64, out=FAKE):
     return L.vsa_block_sics(x, dtype, B, H, D, n, block, out, NULL)
 
 
+def test_mean_pool_validation(L):
+    def pool(x=FAKE, dtype=1, B=1, H=2, D=128, n=100, block=64, out=FAKE):
+        return L.vsa_block_mean_pool(x, dtype, B, H, D, n, block, out, NULL)
+    assert pool(x=NULL) == E_NULL
+    assert pool(out=NULL) == E_NULL
+    assert pool(dtype=5) == E_DTYPE
+    assert pool(n=0) == E_SHAPE
+    assert pool(block=-1) == E_SHAPE
+    assert pool(B=65536) == E_SHAPE
+    assert pool(D=96) == E_UNSUP
+    assert pool(x=ODD) == E_UNSUP
+    assert pool(out=ctypes.c_void_p(0x1004)) == E_UNSUP
+
+
 def test_sics_validation(L):
     assert sics(L, x=NULL) == E_NULL
     assert sics(L, out=NULL) == E_NULL

@@ -59,7 +59,7 @@ def test_attn_flops_dense_closed_form():
     ("path_radial_kernel_stats.md", dict(D=128, block_q=128, block_k=128, grouped=True, heads=24,
                                          n_qblocks=3516)),
     ("path_ar_kernel_stats.md", dict(D=128, block_q=64, block_k=64, grouped=True, heads=12,
-                                     n_qblocks=74)),
+                                     n_qblocks=74, n_kblocks=512)),
 ])
 def test_kernel_label_is_the_profiled_kernel(profile, args):
     """The label the bench line divides by must name the kernel the trace of that

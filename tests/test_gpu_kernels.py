@@ -207,6 +207,24 @@ def test_block_sics_matches_oracle(B, N, H, D, block, dtype):
         assert np.all(np.isclose(got, 1.0, rtol=0, atol=1e-14) | (got == 0.0))
 
 
+# ------------------------------------------------------------ block mean pool
+@pytest.mark.parametrize("B,N,H,D,block,dtype", [
+    (1, 1000, 2, 128, 64, torch.bfloat16),      # ragged last block (40 rows)
+    (2, 300, 3, 64, 7, torch.float32),          # rows split unevenly over the waves
+    (1, 130, 40, 128, 384, torch.bfloat16),     # one short block; 10 vector slices per row
+    (1, 65, 1, 64, 1, torch.bfloat16),          # one-row blocks: the row itself
+    (1, 5000, 24, 128, 128, torch.bfloat16),    # several passes of 16 rows per wave
+])
+def test_block_mean_pool_bit_exact(B, N, H, D, block, dtype):
+    """The pooling pass of the NABLA mask: exact fp64 sums of bf16 rows, one division, so
+    the GPU means equal the oracle's bit for bit (fp32 inputs of this range too)."""
+    x = rand((B, N, H, D), dtype, 33)
+    got = vsa.vsa_block_mean_pool(x.to(DEV), block).cpu().numpy()
+    xn = x.double().numpy()
+    want = np.stack([np.stack([oracle.pool_blocks(xn[b, :, h], block) for h in range(H)]) for b in range(B)])
+    assert got.shape == want.shape and np.array_equal(got, want)
+
+
 # ------------------------------------------------------------ KV compaction
 @pytest.mark.parametrize("B,H,D,nq,nk,bq,bk,slabs,dtype,tail_slabs", [
     (1, 3, 128, 300, 1000, 64, 64, 3, torch.bfloat16, (0, 2)),   # ragged tail kept by two heads
@@ -239,11 +257,16 @@ def test_kv_compaction_matches_oracle(B, H, D, nq, nk, bq, bk, slabs, dtype, tai
     assert np.array_equal(got.numpy() if dtype == torch.float32 else got.view(torch.int16).numpy(), want)
     cc = vsa.vsa_mask_remap(rpd, cid, slabs, nbq, slot, nbk)
     assert np.array_equal(cc.cpu().numpy(), kvcache.mask_remap(rp, ci, remap, nbq)[1])
-    # attention over the compact cache is the same computation, tile for tile
+    # attention over the compact cache is the same computation, tile for tile (compared on the
+    # plain path: with a workspace the plan may split the full cache's longer key range over
+    # workgroups and not the compact one's, which changes the rounding only)
     vc = vsa.vsa_kv_gather(v.to(DEV), slot, slabs, bk, n_out)
-    o_full, l_full = vsa.vsa_block_sparse_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), rpd, cid, bq, bk, slabs)
-    o_comp, l_comp = vsa.vsa_block_sparse_attn_fwd(q.to(DEV), kc, vc, rpd, cc, bq, bk, slabs)
+    o_full, l_full = vsa.vsa_block_sparse_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), rpd, cid, bq, bk, slabs,
+                                                   grouped=False)
+    o_comp, l_comp = vsa.vsa_block_sparse_attn_fwd(q.to(DEV), kc, vc, rpd, cc, bq, bk, slabs, grouped=False)
     assert torch.equal(o_full, o_comp) and torch.equal(l_full, l_comp)
+    o_ws, _ = vsa.vsa_block_sparse_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), rpd, cid, bq, bk, slabs)
+    assert (o_ws.float() - o_comp.float()).abs().max() <= (BF16_MAX if dtype == torch.bfloat16 else F32_MAX)
 
 
 # -------------------------------------------------------------- backward
@@ -350,6 +373,109 @@ def test_grouped_query_blocks(case):
         errs.append(np.abs(o_g[b, rows, h].cpu().double().numpy() - ref))
     err = np.concatenate(errs)
     assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN
+
+
+# ------------------------------------------------ groups across frames (radial)
+@pytest.mark.parametrize("T,S,block,H,per_head", [
+    (12, 1000, 128, 16, False),   # 7.8 blocks per frame: groups 7 blocks apart, a ragged last block
+    (9, 768, 64, 40, True),       # 12 blocks per frame, 64-row blocks (two tiles per stage), per-head masks
+    (40, 300, 128, 8, False),     # 2.3 blocks per frame: groups 2 apart
+])
+def test_radial_grouping_across_frames(T, S, block, H, per_head):
+    """vsa_radial_attn_fwd groups query blocks at the same place of consecutive frames; it
+    computes the same thing as the plain forward (bit for bit for 65- to 128-row blocks,
+    whose rows walk the same tiles in the same order), with the radial mask or any other."""
+    n = T * S
+    nb = -(-n // block)
+    q, k, v = (rand((1, n, H, 128), torch.bfloat16, 95 + i) for i in range(3))
+    if per_head:
+        rng = np.random.default_rng(96)
+        keep = rng.random((H * nb, nb)) < 0.4
+        keep[np.arange(H * nb), rng.integers(0, nb, size=H * nb)] = True
+        keep[1] = False
+        rp_h, ci_h = oracle.csr_from_bool(keep)
+        rp, ci = torch.from_numpy(rp_h).to(DEV), torch.from_numpy(ci_h).to(DEV)
+        slabs = H
+    else:
+        rp, ci = vsa.vsa_mask_radial(T, S, block, DEV)
+        rp_h, ci_h = csr_np(rp, ci)
+        slabs = 1
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    assert vsa.attn_fwd_workspace_bytes_radial(qd, kd, rp, ci, block, S, slabs) > 0      # it groups
+    o_f, l_f = vsa.vsa_radial_attn_fwd(qd, kd, vd, rp, ci, block, S, slabs)
+    o_p, l_p = vsa.vsa_block_sparse_attn_fwd(qd, kd, vd, rp, ci, block, block, slabs)
+    if block > 64:
+        assert torch.equal(o_f, o_p) and torch.equal(l_f, l_p)
+    else:
+        assert (o_f.float() - o_p.float()).abs().max() <= BF16_MAX
+    rng = np.random.default_rng(97)
+    errs = []
+    for h in (0, H - 1):
+        rows = np.concatenate([rng.choice(n, 96, replace=False), [n - 1]])
+        base = 0 if slabs == 1 else h * nb
+        ref, _ = oracle.attention_rows(to_np(q[0, rows, h]), rows, to_np(k[0, :, h]), to_np(v[0, :, h]),
+                                       rp_h, ci_h, base, block, block, 128 ** -0.5)
+        errs.append(np.abs(o_f[0, rows, h].cpu().double().numpy() - ref))
+    err = np.concatenate(errs)
+    assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN
+
+
+# ------------------------------------------------------- split key streams
+SPLIT_CASES = [
+    # batch, heads, D, nq, nk, bq, bk, density, per-head masks
+    (1, 4, 128, 2000, 3000, 64, 64, 0.5, True),      # 4-wave key split; ragged last query and key blocks
+    (1, 2, 128, 1000, 5000, 128, 128, 0.6, False),   # 4 waves per 128-row block
+    (2, 1, 64, 777, 9000, 384, 384, 0.7, True),      # 12-wave blocks; chunks of unequal length
+    (1, 6, 128, 4680, 32760, 64, 64, 0.22, True),    # half the heads of the autoregressive chunk step
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[str(i) for i in range(len(SPLIT_CASES))])
+def test_split_key_streams(case):
+    """Too few rows to fill the chip: each row's kept-block list is split over several
+    workgroups and merged.  The result matches the oracle, equals the unsplit run to
+    rounding, is the same on a second call, and an empty row still gives 0 and -inf."""
+    B, H, D, nq, nk, bq, bk, dens, per_head = case
+    slabs = B * H if per_head else 1
+    scale = D ** -0.5
+    q, k, v = rand((B, nq, H, D), torch.bfloat16, 90), rand((B, nk, H, D), torch.bfloat16, 91), \
+        rand((B, nk, H, D), torch.bfloat16, 92)
+    nbq, nbk = -(-nq // bq), -(-nk // bk)
+    rng = np.random.default_rng(93)
+    keep = rng.random((slabs * nbq, nbk)) < dens
+    keep[:, -1] |= rng.random(slabs * nbq) < 0.5                     # the ragged key block
+    keep[np.arange(slabs * nbq), rng.integers(0, nbk, size=slabs * nbq)] = True
+    keep[1] = False                                                    # an empty row
+    keep[2, :3] = True                                                 # a short row: chunks may be empty
+    keep[2, 3:] = False
+    rp, ci = oracle.csr_from_bool(keep)
+    rpd, cid = torch.from_numpy(rp).to(DEV), torch.from_numpy(ci).to(DEV)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    label = __import__("bench").attn_kernel_name(D, bq, bk, True, B, H, nbq, False, nbk)
+    assert label.endswith("true>"), label                             # this case does split
+    o_s, l_s = vsa.vsa_block_sparse_attn_fwd(qd, kd, vd, rpd, cid, bq, bk, slabs, scale)
+    o_s2, l_s2 = vsa.vsa_block_sparse_attn_fwd(qd, kd, vd, rpd, cid, bq, bk, slabs, scale)
+    assert torch.equal(o_s, o_s2) and torch.equal(l_s, l_s2)
+    o_u, l_u = vsa.vsa_block_sparse_attn_fwd(qd, kd, vd, rpd, cid, bq, bk, slabs, scale, grouped=False)
+    assert (o_s.float() - o_u.float()).abs().max() <= BF16_MAX
+    assert torch.allclose(l_s, l_u, rtol=0, atol=1e-4, equal_nan=False) or \
+        torch.equal(torch.isinf(l_s), torch.isinf(l_u))
+    errs = []
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        rows = np.concatenate([np.arange(0, 3 * bq), rng.choice(nq, 64, replace=False), [nq - 1]])
+        rows = rows[rows < nq]
+        base = 0 if slabs == 1 else (b * H + h) * nbq
+        ref, ref_lse = oracle.attention_rows(to_np(q[b, rows, h]), rows, to_np(k[b, :, h]), to_np(v[b, :, h]),
+                                             rp, ci, base, bq, bk, scale)
+        errs.append(np.abs(o_s[b, rows, h].cpu().double().numpy() - ref))
+        got_lse = l_s[b, h, rows].cpu().double().numpy()
+        fin = np.isfinite(ref_lse)
+        assert np.array_equal(np.isfinite(got_lse), fin)
+        assert np.abs(got_lse[fin] - ref_lse[fin]).max() < 2e-2
+    err = np.concatenate(errs)
+    assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN
+    if slabs > 1 or nbq > 1:                                           # the empty row: zeros
+        assert torch.all(o_s[0, bq:min(2 * bq, nq), 0] == 0)
 
 
 # ------------------------------------------------------------- tiled forward

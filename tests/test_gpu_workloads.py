@@ -65,9 +65,10 @@ def _sampled_rows_check(name, x_cpu, o_gpu, rp, ci, block_q, block_k, n_slabs, p
     return err.max(), err.mean()
 
 
-def _run_path(x, grid, tile, mask_fn, block, n_slabs, fused=False):
+def _run_path(x, grid, tile, mask_fn, block, n_slabs, fused=False, frame_tokens=None):
     """reorder (if tiled) -> mask -> attention -> inverse reorder, on the GPU; fused: the
-    mask, then the attention on raster-order tokens with the reorder folded in."""
+    mask, then the attention on raster-order tokens with the reorder folded in; with
+    frame_tokens, the attention groups query blocks across frames (vsa_radial_attn_fwd)."""
     qd, kd, vd = (x[w].to(DEV) for w in ("q", "k", "v"))
     if fused:
         rp, ci = mask_fn(None, None)
@@ -77,7 +78,7 @@ def _run_path(x, grid, tile, mask_fn, block, n_slabs, fused=False):
     if tile is not None:
         qd, kd, vd = (vsa.vsa_tile_reorder(t, grid, tile) for t in (qd, kd, vd))
     rp, ci = mask_fn(qd, kd)
-    o, lse = vsa.vsa_block_sparse_attn_fwd(qd, kd, vd, rp, ci, block, block, n_slabs)
+    o, lse = vsa.vsa_block_sparse_attn_fwd(qd, kd, vd, rp, ci, block, block, n_slabs, frame_tokens=frame_tokens)
     if tile is not None:
         o = vsa.vsa_tile_reorder(o, grid, tile, inverse=True)
     torch.cuda.synchronize()
@@ -173,7 +174,8 @@ def test_radial_workload():
     t0 = time.time()
     x = gen.make_inputs("radial")
     log(f"radial: inputs {time.time() - t0:.1f}s")
-    o, rp_d, ci_d = _run_path(x, None, None, lambda q, k: vsa.vsa_mask_radial(T, S, block, DEV), block, 1)
+    o, rp_d, ci_d = _run_path(x, None, None, lambda q, k: vsa.vsa_mask_radial(T, S, block, DEV), block, 1,
+                              frame_tokens=S)
     rp, ci = csr_np(rp_d, ci_d)
     orp, oci = oracle.mask_radial(T, S, block)
     assert np.array_equal(rp, orp) and np.array_equal(ci, oci) and len(ci) == 2718652
