@@ -9,7 +9,7 @@ from ._lib import (  # noqa: F401
     EXPORTS, LIB_PATH, VSA_BF16, VSA_F32, VsaError, all_ones_mask, ar_forced_ranges, lib,
     nabla_workspace_bytes, sta_capacity, status_string, vsa_block_sparse_attn_fwd, vsa_block_sparse_attn_bwd,
     attn_bwd_workspace_bytes, attn_fwd_workspace_bytes, vsa_tiled_attn_fwd, tiled_attn_workspace_bytes,
-    vsa_radial_attn_fwd, attn_fwd_workspace_bytes_radial,
+    vsa_radial_attn_fwd, attn_fwd_workspace_bytes_radial, vsa_block_sparse_attn_fwd_static,
     vsa_mask_nabla, vsa_mask_radial, vsa_mask_sta, vsa_tile_reorder,
     sta_heads_capacity, vsa_mask_sta_heads, vsa_mask_union, vsa_block_sics, vsa_block_mean_pool,
     compact_tokens, vsa_kv_compact, vsa_kv_gather, vsa_kv_plan, vsa_mask_remap,

@@ -48,6 +48,8 @@ _SIGS = {
                         ctypes.POINTER(Select), _P, _P, _I64, _P, ctypes.POINTER(ctypes.c_size_t), _P], _I32),
     "vsa_block_sparse_attn_fwd": ([_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I64, _I64, _I32, _I32,
                                    _P, _P, _I32, _F32, _P, ctypes.POINTER(ctypes.c_size_t), _P], _I32),
+    "vsa_block_sparse_attn_fwd_static": ([_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I64, _I64, _I32, _I32,
+                                          _P, _P, _I32, _F32, _P], _I32),
     "vsa_radial_attn_fwd": ([_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I64, _I64, _I32, _I32, _I64,
                              _P, _P, _I32, _F32, _P, ctypes.POINTER(ctypes.c_size_t), _P], _I32),
     "vsa_tiled_attn_fwd": ([_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
@@ -405,6 +407,22 @@ def vsa_mask_nabla(q, k, block_q, block_k, scale=None, threshold=None, topk=0, f
                                 _ptr(col_idx), col_idx.numel(), _ptr(workspace), ctypes.byref(nbytes),
                                 _stream(q)), "vsa_mask_nabla")
     return row_ptr, col_idx
+
+
+def vsa_block_sparse_attn_fwd_static(q, k, v, row_ptr, col_idx, block_q, block_k, out, lse, n_slabs=1, scale=None):
+    """vsa_block_sparse_attn_fwd with its workspace in the library's fixed device array:
+    nothing is allocated (out and lse are the caller's).  Calls that overlap on one GPU race."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("row_ptr", row_ptr), ("col_idx", col_idx), ("out", out)):
+        _require(t, name, q.device)
+    if lse is not None:
+        _require(lse, "lse", q.device)
+    B, nq, Hh, D = q.shape
+    scale = D ** -0.5 if scale is None else scale
+    _check(lib().vsa_block_sparse_attn_fwd_static(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _DTYPE[q.dtype], B,
+                                                  Hh, D, nq, k.shape[1], block_q, block_k, _ptr(row_ptr),
+                                                  _ptr(col_idx), n_slabs, float(scale), _stream(q)),
+           "vsa_block_sparse_attn_fwd_static")
+    return out, lse
 
 
 def vsa_radial_attn_fwd(q, k, v, row_ptr, col_idx, block, frame_tokens, n_slabs=1, scale=None, out=None, lse=None,

@@ -3,11 +3,40 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/vsa.h"
 #include "vsa_internal.h"
 
+// Workspace of vsa_block_sparse_attn_fwd_static, for callers that cannot allocate: one
+// array on every GPU the library runs on, held until the process ends.  Host code never
+// uses the array's name as an address: static_scratch() resolves the device address.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
 namespace {
+
+// The device address of `scratch` on the current device, resolved once per device with
+// that device current (each GPU holds its own copy at its own address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 constexpr int64_t kI32Max = 2147483647;
 
@@ -252,7 +281,7 @@ vsa_status attn_fwd_untiled(const void* q, const void* k, const void* v, void* o
                             int64_t batch, int32_t heads, int32_t head_dim, int64_t nq, int64_t nk,
                             int32_t block_q, int32_t block_k, const int32_t* row_ptr, const int32_t* col_idx,
                             int32_t n_slabs, float scale, int group_stride, void* workspace,
-                            size_t* workspace_bytes, hipStream_t stream) {
+                            size_t* workspace_bytes, hipStream_t stream, bool use_static = false) {
   if (!q || !k || !v || !o || !row_ptr || !col_idx) return VSA_ERR_NULL;
   vsa_status st = check_tokens(dtype, batch, heads, head_dim, nq, nk, block_q, block_k);
   if (st != VSA_OK) return st;
@@ -263,6 +292,16 @@ vsa_status attn_fwd_untiled(const void* q, const void* k, const void* v, void* o
                   row_ptr, col_idx, n_slabs, scale};
   a.group_stride = group_stride;
   const size_t want = dtype == VSA_BF16 ? vsa::attn_fwd_workspace(a) : 0;
+  if (use_static) {  // the file-scope scratch array, never an allocation
+    if (want > kStaticScratchBytes) return VSA_ERR_CAPACITY;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return VSA_ERR_UNSUPPORTED;
+    void* ws = nullptr;
+    if (want > 0) {
+      const hipError_t e = static_scratch(&ws);
+      if (e != hipSuccess) return VSA_ERR_HIP;
+    }
+    return from_hip(vsa::launch_attn_fwd(a, ws, ws ? kStaticScratchBytes : 0, stream));
+  }
   if (workspace_bytes && !workspace) {  // size query
     *workspace_bytes = want;
     return VSA_OK;
@@ -286,6 +325,15 @@ vsa_status vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v
                                      hipStream_t stream) {
   return attn_fwd_untiled(q, k, v, o, lse, dtype, batch, heads, head_dim, nq, nk, block_q, block_k, row_ptr,
                           col_idx, n_slabs, scale, 1, workspace, workspace_bytes, stream);
+}
+
+vsa_status vsa_block_sparse_attn_fwd_static(const void* q, const void* k, const void* v, void* o, float* lse,
+                                            int32_t dtype, int64_t batch, int32_t heads, int32_t head_dim,
+                                            int64_t nq, int64_t nk, int32_t block_q, int32_t block_k,
+                                            const int32_t* row_ptr, const int32_t* col_idx, int32_t n_slabs,
+                                            float scale, hipStream_t stream) {
+  return attn_fwd_untiled(q, k, v, o, lse, dtype, batch, heads, head_dim, nq, nk, block_q, block_k, row_ptr,
+                          col_idx, n_slabs, scale, 1, nullptr, nullptr, stream, true);
 }
 
 vsa_status vsa_radial_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t dtype,

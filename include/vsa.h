@@ -27,7 +27,8 @@
  *   ("one slab"); a per-(batch, head) mask has n_rows = batch * heads * n_qblocks
  *   with row r = (b * heads + h) * n_qblocks + qblock.
  * - Ownership: the caller owns every buffer.  The library allocates no device
- *   memory, holds no mutable global state and is reentrant.  Pointers are borrowed
+ *   memory, holds no mutable global state and is reentrant (except
+ *   vsa_block_sparse_attn_fwd_static, whose workspace is a fixed device array).  Pointers are borrowed
  *   until the work enqueued on `stream` completes; every call is asynchronous and
  *   returns once its kernels are enqueued.
  * - Errors: every argument is validated on the host before anything is launched;
@@ -340,6 +341,31 @@ vsa_status vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v
                                      int32_t n_slabs, float scale,
                                      void* workspace, size_t* workspace_bytes,
                                      hipStream_t stream);
+
+/*
+ * vsa_block_sparse_attn_fwd_static -- vsa_block_sparse_attn_fwd with no workspace
+ * argument and no allocation, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * The workspace the forward would ask for (union lists of grouped query blocks, or
+ * the partial outputs of split key streams) is taken from a 64 MiB array that the
+ * library holds on every GPU it runs on until the process ends; every other argument
+ * and the result are those of vsa_block_sparse_attn_fwd with a workspace.  The array
+ * is state shared by every call on a GPU: calls that overlap on one GPU (two streams,
+ * or two threads) race and must be serialised by the caller.  Nothing in it needs to
+ * start at zero (every value is written before it is read), and it keeps the last
+ * call's contents.  The call allocates nothing: no hipMalloc, hipFree or allocating
+ * library routine.
+ * Errors: as for vsa_block_sparse_attn_fwd; VSA_ERR_CAPACITY (checked before anything
+ * touches the device) when the problem needs more than 64 MiB of workspace (query it
+ * with vsa_block_sparse_attn_fwd and workspace = NULL).
+ */
+vsa_status vsa_block_sparse_attn_fwd_static(const void* q, const void* k, const void* v, void* o,
+                                            float* lse, int32_t dtype, int64_t batch, int32_t heads,
+                                            int32_t head_dim, int64_t nq, int64_t nk, int32_t block_q,
+                                            int32_t block_k, const int32_t* row_ptr,
+                                            const int32_t* col_idx, int32_t n_slabs, float scale,
+                                            hipStream_t stream);
 
 /*
  * vsa_radial_attn_fwd -- the forward above, for masks over raster-order frames, with

@@ -147,6 +147,21 @@ def test_attn_validation(L):
     assert attn(L, H=65536, D=128, dtype=0, query=True)[0] == OK      # fp32 path: no such limit
 
 
+def test_static_attn_validation(L):
+    """The allocation-free forward validates like the forward and refuses a problem whose
+    workspace would exceed its 64 MiB array before it touches the device."""
+    def st(q=FAKE, H=2, n=100, b=64, slabs=1, scale=0.1, dtype=1):
+        return L.vsa_block_sparse_attn_fwd_static(q, FAKE, FAKE, FAKE, NULL, dtype, 1, H, 128, n, n, b, b, FAKE, FAKE,
+                                                  slabs, scale, NULL)
+    assert st(q=NULL) == E_NULL
+    assert st(dtype=4) == E_DTYPE
+    assert st(slabs=3) == E_PARAM
+    assert st(scale=0.0) == E_PARAM
+    assert st(q=ODD) == E_UNSUP
+    # 256 heads x 30,000 tokens in 64-token blocks, per-head masks: 75.9 MB of union lists
+    assert st(H=256, n=30000, slabs=256) == E_CAP
+
+
 def tiled(L, q=FAKE, dtype=1, B=1, H=2, D=128, grid=(12, 16, 16), tile=(6, 8, 8), rp=FAKE, ci=FAKE, slabs=1,
           scale=0.1, query=False):
     nb = ctypes.c_size_t(123)
