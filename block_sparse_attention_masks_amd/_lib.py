@@ -10,7 +10,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libvsa.so")
+# VSA_LIB names another build of the same library (e.g. the host-sanitized one); default: in-tree
+LIB_PATH = os.environ.get("VSA_LIB") or os.path.join(_PKG, "libvsa.so")
 
 VSA_F32, VSA_BF16 = 0, 1
 _DTYPE = {torch.float32: VSA_F32, torch.bfloat16: VSA_BF16}

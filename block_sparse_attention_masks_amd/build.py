@@ -1,6 +1,6 @@
 """Build libvsa.so (the HIP kernels and their C ABI) for gfx950, in-tree.
 
-Usage: python -m block_sparse_attention_masks_amd.build  [-v]
+Usage: python -m block_sparse_attention_masks_amd.build  [-v] [--sanitize]
 Every .hip file under csrc/ is compiled by hipcc to an object, in parallel, and
 the objects are linked into block_sparse_attention_masks_amd/libvsa.so.
 """
@@ -36,19 +36,35 @@ def _run(cmd, verbose):
         print("\n".join(msgs), file=sys.stderr)
 
 
-def build(verbose=False):
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for the argument-validation layer
+# (the device code is built as usual): each flag applies to the host compilation only.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+            "-Xarch_host", "-g"]
+SANITIZED_LIB = os.path.join(PKG, "_build", "sanitize", "libvsa.so")
+
+
+def build(verbose=False, sanitize=False):
+    """Compile every csrc/*.hip for gfx950 and link libvsa.so in the package directory.  With
+    sanitize=True the host code is instrumented and the library goes to _build/sanitize/ instead:
+    point VSA_LIB at it and preload the ASan runtime into the (uninstrumented) interpreter, with
+    ASAN_OPTIONS=detect_leaks=0 since CPython's own allocations are not freed at exit."""
     srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
-    out_dir = os.path.join(PKG, "_build")
+    out_dir = os.path.join(PKG, "_build", "sanitize") if sanitize else os.path.join(PKG, "_build")
     os.makedirs(out_dir, exist_ok=True)
+    flags = FLAGS + (SANITIZE if sanitize else [])
     objs = [os.path.join(out_dir, os.path.basename(s)[:-4] + ".o") for s in srcs]
     with ThreadPoolExecutor(min(8, len(srcs))) as ex:
-        list(ex.map(lambda so: _run([HIPCC, *FLAGS, "-c", so[0], "-o", so[1]], verbose),
+        list(ex.map(lambda so: _run([HIPCC, *flags, "-c", so[0], "-o", so[1]], verbose),
                     zip(srcs, objs)))
-    tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    lib = SANITIZED_LIB if sanitize else LIB
+    tmp = lib + ".tmp"
+    link = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libasan"] \
+        if sanitize else []
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *link, "-o", tmp, *objs], verbose)
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))
