@@ -85,7 +85,7 @@ def attn_flops(rp, ci, block_q, block_k, nq, nk, D, bh, n_slabs):
 
 
 def attn_kernel_name(D, block_q, block_k, grouped=False, batch=1, heads=1, n_qblocks=1, tiled=False,
-                     n_kblocks=0):
+                     n_kblocks=0, nq=0, nk=1):
     """Label of the bf16 instantiation the library launches (its plan, mirrored here).  With a
     workspace (grouped=True), query blocks of <= 128 rows are grouped into 12-, 8- or 4-wave
     workgroups, the first width whose group count keeps enough workgroups; otherwise it picks
@@ -93,8 +93,10 @@ def attn_kernel_name(D, block_q, block_k, grouped=False, batch=1, heads=1, n_qbl
     workspace, splits each row's key stream into chunks when the rows cannot fill one round
     of workgroups.  Template arguments: head_dim, key split, waves, grouped, tiled
     (raster-order tokens with the tiles as blocks), stream tiles per LDS stage (two for
-    grouped, untiled key blocks of <= 64), split key streams."""
+    grouped, untiled key blocks of <= 64), split key streams, V packed transposed (with a
+    workspace, key blocks of a multiple of 64 and nq >= nk)."""
     tl = str(tiled).lower()
+    vt = str(bool(grouped and block_k % 64 == 0 and nq >= nk)).lower()
     if grouped:
         wpb = -(-block_q // 32)
         for nw in (12, 8, 4):
@@ -103,14 +105,14 @@ def attn_kernel_name(D, block_q, block_k, grouped=False, batch=1, heads=1, n_qbl
                 continue
             if batch * heads * -(-n_qblocks // G) >= (512 if nw == 4 else 256):
                 tw = 2 if nw >= 8 and block_k <= 64 and not tiled else 1
-                return f"attn_fwd_bf16_kernel<{D}, 1, {nw}, true, {tl}, {tw}, false>"
+                return f"attn_fwd_bf16_kernel<{D}, 1, {nw}, true, {tl}, {tw}, false, {vt}>"
     ks = 2 if block_q <= 64 else 1
     nw = 4 if ks == 2 else (12 if block_q % 384 == 0 else (8 if block_q % 256 == 0 else 4))
     items = batch * heads * n_qblocks * -(-block_q // (32 * nw // ks))
     slots = 256 * (2 if nw == 4 else 1)
-    n = min(-(-4 * slots // items), 8, n_kblocks // 8)
+    n = min(-(-2 * slots // items), 8, n_kblocks // 8)
     sp = grouped and items < slots and n_kblocks >= 16 and n >= 2
-    return f"attn_fwd_bf16_kernel<{D}, {ks}, {nw}, false, {tl}, 1, {str(sp).lower()}>"
+    return f"attn_fwd_bf16_kernel<{D}, {ks}, {nw}, false, {tl}, 1, {str(sp).lower()}, {vt}>"
 
 
 def source_hash(path):
@@ -695,7 +697,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": attn_kernel_name(path.D, path.bq, path.bk, path.ws is not None,
-                                                                 path.B, path.H, path.nbq, path.fused, path.nbk),
+                                                                 path.B, path.H, path.nbq, path.fused, path.nbk,
+                                                                 path.nq, path.nk),
                      "flops_per_launch": flops, "ms_per_launch": round(attn_ms, 4),
                      # the same fraction against the peak scaled to the mean clock sampled in
                      # the timed steps (the published peak assumes 2.4 GHz)

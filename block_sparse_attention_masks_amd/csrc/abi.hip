@@ -293,7 +293,8 @@ vsa_status attn_fwd_untiled(const void* q, const void* k, const void* v, void* o
   a.group_stride = group_stride;
   const size_t want = dtype == VSA_BF16 ? vsa::attn_fwd_workspace(a) : 0;
   if (use_static) {  // the file-scope scratch array, never an allocation
-    if (want > kStaticScratchBytes) return VSA_ERR_CAPACITY;
+    // the packed V^T is optional: it is used only when the scratch holds it too
+    if (dtype == VSA_BF16 && vsa::attn_fwd_workspace_min(a) > kStaticScratchBytes) return VSA_ERR_CAPACITY;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return VSA_ERR_UNSUPPORTED;
     void* ws = nullptr;
     if (want > 0) {

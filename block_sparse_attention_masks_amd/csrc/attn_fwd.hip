@@ -28,10 +28,20 @@
 //     keeps every exponent <= 2^8 and leaves the normalised result unchanged;
 //   * O^T += V^T P^T on the same instruction (M = head dim, N = queries, K =
 //     keys), P rounded to bf16; the row sum adds the rounded values, so the
-//     weights applied to V are exactly normalised.  V stays row-major in LDS; ds_read_b64_tr_b16
-//     delivers each lane its 8 keys of one head-dim column.  The key order inside
-//     each 16-key group follows the S accumulator layout (lane half g holds keys
-//     4g..4g+3 and 8+4g..8+4g+3), so P feeds the product without any shuffle.
+//     weights applied to V are exactly normalised.  Two V layouts (VT):
+//       - VT: V was packed transposed, [batch, heads, 64-key tile, D, 64] (vt_pack_kernel,
+//         one HBM pass), so a tile is one contiguous D x 64 block and a lane's 8 keys of one
+//         head-dim row are 16 contiguous bytes: the A operand is a plain ds_read_b128.  The
+//         K rows are read into the S product in a permuted order (bits 2 and 3 of the row
+//         swapped) so that lane half g's P values are keys 8g..8g+7 of each 16-key group;
+//       - else V stays row-major in LDS and ds_read_b64_tr_b16 delivers each lane its 8
+//         keys of one head-dim column, in the order of the S accumulator layout (lane half
+//         g holds keys 4g..4g+3 and 8+4g..8+4g+3).
+//     Either way P feeds the product without any shuffle.  VT halves the LDS time of the V
+//     reads (a 64-bit read moves half the bytes per cycle of a 128-bit one) and lets the
+//     compiler schedule them, where the transposed reads need their wait in the same asm
+//     block.  It needs a workspace for the packed copy and blocks of a multiple of 64 keys
+//     (every tile then starts at a multiple of 64; tiled, the copy is in tile-major order).
 // Ragged key tails are masked with -inf; query rows past the block or the
 // sequence are computed but never stored.  A row with no kept block writes 0
 // and lse = -inf.  Tiled (TL): q, k, v, o and lse are in raster order of a 3D grid
@@ -43,6 +53,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <cstdint>
 #include <type_traits>
 
 #include "group_union.h"
@@ -204,6 +215,14 @@ __device__ inline float xchg32(float x, int g) {
 //     quarter of the banks.
 template <int D> __device__ inline int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 template <int D> __device__ inline int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+//   * V^T (VT): row d of the tile (its 64 keys, 128 bytes, 8 chunks) at d * 64 elements,
+//     chunk c at slot c ^ swz_vt(d).  A V-fragment read touches 32 consecutive rows at one
+//     chunk; any 16 consecutive rows, 8 of each parity, land on distinct banks.
+__device__ inline int swz_vt(int r) { return (r >> 1) & 7; }
+// VT: key row of the tile that A-operand row c (0..31) of the S product reads: bits 2 and 3
+// of c swapped.  The accumulator then holds, in lane half g, keys 16 j + 8 g + (a & 7) for
+// element a of the 16, j = a >> 3 (without it: 8 (a >> 2) + 4 g + (a & 3)).
+__device__ inline int kperm(int c) { return (c & ~12) | ((c & 4) << 1) | ((c & 8) >> 1); }
 
 // s_waitcnt vmcnt(N), leaving the other counters alone (gfx9 encoding: vmcnt low
 // bits [3:0] and high bits [15:14], expcnt [6:4], lgkmcnt [11:8]).
@@ -291,7 +310,7 @@ struct Smem {
   uint16_t v[2 * TW][kBN * D];
 };
 
-template <int D, int KS, int NW, bool GR, bool TL, int TW, bool SP>
+template <int D, int KS, int NW, bool GR, bool TL, int TW, bool SP, bool VT>
 __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
@@ -369,20 +388,30 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
   if constexpr (TL) it.open(tg);
   else it.open();
   const uint16_t* kbase = k + (b * nk * heads + h) * (int64_t)D;
-  const uint16_t* vbase = v + (b * nk * heads + h) * (int64_t)D;
+  // VT: v is the packed V^T, one D x 64 block per (batch, head, 64-key tile)
+  const uint16_t* vbase = VT ? v + (b * heads + h) * ((nk + kBN - 1) / kBN) * (int64_t)(D * kBN)
+                             : v + (b * nk * heads + h) * (int64_t)D;
 
   // Copy plan: wave-load c = w + NW j (c < 2 CB) moves RPC rows of K (c < CB) or of V
   // (chunk-block c - CB) of the tile; the tile base is wave-uniform, each lane adds a
   // loop-invariant row and chunk.  Rows past the last key repeat it (masked later).
   const uint32_t row_bytes = 2u * (uint32_t)row_stride;
+  // VT: a V wave-load c - CB moves head-dim rows 8 (c - CB) .. + 7 of the tile's D x 64
+  // block (8 chunks of 16 bytes each); ch16 is then the lane's whole byte offset in the block
   int lrow[NJ];
   uint32_t ch16[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int c = w + NW * j;
     const int cb = c < CB ? c : c - CB;
-    lrow[j] = cb * RPC + l / SPR;
-    ch16[j] = 16u * ((l % SPR) ^ (c < CB ? swz_k<D>(lrow[j]) : swz_v<D>(lrow[j])));
+    if (VT && c >= CB) {
+      const int d = cb * 8 + l / 8;
+      lrow[j] = 0;
+      ch16[j] = 128u * d + 16u * ((l % 8) ^ swz_vt(d));
+    } else {
+      lrow[j] = cb * RPC + l / SPR;
+      ch16[j] = 16u * ((l % SPR) ^ (c < CB ? swz_k<D>(lrow[j]) : swz_v<D>(lrow[j])));
+    }
   }
   int loff[NJ];  // tiled: lane part of row lrow[j] of a full copy tile
 #pragma unroll
@@ -399,12 +428,15 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
       // call checks that a copy tile's rows lie within 2^32 bytes and 2^24 rows of it)
       const int64_t r0 = t_.rb + t_.uo;
       const char* kt = (const char*)(kbase + r0 * row_stride);
-      const char* vt = (const char*)(vbase + r0 * row_stride);
+      // VT: the packed copy is in tile-major key order, so the tile is k0 / 64 as untiled
+      const char* vt = VT ? (const char*)(vbase + (int64_t)(k0 / kBN) * (D * kBN))
+                          : (const char*)(vbase + r0 * row_stride);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int c = w + NW * j;
         if (c < 2 * CB) {
-          const uint32_t ro = __umul24((uint32_t)(lrow[j] <= last ? loff[j] : 0), row_bytes) + ch16[j];
+          const uint32_t ro = VT && c >= CB ? ch16[j]
+                                            : __umul24((uint32_t)(lrow[j] <= last ? loff[j] : 0), row_bytes) + ch16[j];
           if (c < CB)
             load_lds16((const uint16_t*)(kt + ro), sm.k[stage] + c * 512);
           else
@@ -413,12 +445,14 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
       }
     } else {
       const char* kt = (const char*)(kbase + (int64_t)k0 * row_stride);
-      const char* vt = (const char*)(vbase + (int64_t)k0 * row_stride);
+      // VT: k0 is a multiple of 64; keys past nk are zeros of the packed copy
+      const char* vt = VT ? (const char*)(vbase + (int64_t)(k0 / kBN) * (D * kBN))
+                          : (const char*)(vbase + (int64_t)k0 * row_stride);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int c = w + NW * j;
         if (c < 2 * CB) {
-          const uint32_t ro = __umul24((uint32_t)min(lrow[j], last), row_bytes) + ch16[j];
+          const uint32_t ro = VT && c >= CB ? ch16[j] : __umul24((uint32_t)min(lrow[j], last), row_bytes) + ch16[j];
           if (c < CB)
             load_lds16((const uint16_t*)(kt + ro), sm.k[stage] + c * 512);
           else
@@ -455,7 +489,12 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
     for (int a = 0; a < 16; ++a) acc_o[t][a] = 0.f;
   float m_ref = -INFINITY, l_run = 0.f;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  const int kx = g ^ swz_k<D>(col);   // K slot of (row 32 st + col, chunk 2 kd + g) = (2 kd) ^ kx
+  // the K row this lane's A-operand row reads (VT: permuted), and its slot:
+  // K slot of (row 32 st + krow, chunk 2 kd + g) = (2 kd) ^ kx
+  const int krow = VT ? kperm(col) : col;
+  const int kx = g ^ swz_k<D>(krow);
+  // VT: V slot of (head-dim row 32 t + col, chunk 4 kh + 2 kk + g) = (2 kk) ^ vxg
+  const int vxg = (4 * kh) ^ g ^ swz_vt(col);
   const int jv = (l & 15) >> 2, c4 = l & 3, m2 = (l >> 4) & 1;
   int voff[D / 32];
 #pragma unroll
@@ -505,7 +544,7 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
     for (int kd = 0; kd < D / 16; ++kd)
 #pragma unroll
       for (int st = 0; st < NST; ++st)
-        kf[kd][st] = *(const bf16x8*)(sk + (32 * (kh + st) + col) * D + 8 * ((2 * kd) ^ kx));
+        kf[kd][st] = *(const bf16x8*)(sk + (32 * (kh + st) + krow) * D + 8 * ((2 * kd) ^ kx));
 #pragma unroll
     for (int kd = 0; kd < D / 16; ++kd)
 #pragma unroll
@@ -513,12 +552,12 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
         s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kd][st], qf[kd], s[st], 0, 0, 0);
     if (valid < kBN) {
       asm volatile("" ::: "memory");
-      const int lim = valid - 4 * g - 32 * kh;  // key index minus its lane part
+      const int lim = valid - (VT ? 8 : 4) * g - 32 * kh;  // key index minus its lane part
 #pragma unroll
       for (int st = 0; st < NST; ++st)
 #pragma unroll
         for (int a = 0; a < 16; ++a)
-          if (32 * st + 8 * (a >> 2) + (a & 3) >= lim) s[st][a] = -INFINITY;
+          if (32 * st + (VT ? 16 * (a >> 3) + (a & 7) : 8 * (a >> 2) + (a & 3)) >= lim) s[st][a] = -INFINITY;
     }
     float mx = s[0][0];
     if constexpr (NST == 2) {
@@ -561,7 +600,13 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
 #pragma unroll
     for (int kk = 0; kk < 2 * NST; ++kk) {
       bf16x8 vf[D / 32];
-      read_v_step<D>(vf, lds_addr(sv + 16 * (2 * kh + kk) * D), voff);
+      if constexpr (VT) {
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+          vf[t] = *(const bf16x8*)(sv + (32 * t + col) * kBN + 8 * ((2 * kk) ^ vxg));
+      } else {
+        read_v_step<D>(vf, lds_addr(sv + 16 * (2 * kh + kk) * D), voff);
+      }
 #pragma unroll
       for (int t = 0; t < D / 32; ++t)
         acc_o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t], pf[kk], acc_o[t], 0, 0, 0);
@@ -650,6 +695,40 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
     if (lse != nullptr && g == 0)
       lse[(b * heads + h) * nq + my_row] =
           l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f : -INFINITY;
+  }
+}
+
+// V^T packing for the VT forward: v [batch, nk, heads, D] -> vt [batch, heads, ceil(nk / 64),
+// D, 64], keys past nk zero; tiled (TL), key p of the packed order is raster row
+// raster_row(p), so the copy is in tile-major order.  Workgroup = one (batch, head, 64-key
+// tile); thread = 8 keys x 8 head-dim columns (16-byte loads of 8 key rows, an 8 x 8 transpose
+// in registers, 16-byte stores of 8 head-dim rows).  One HBM read and one write of V.
+template <int D, bool TL>
+__global__ __launch_bounds__(D) void vt_pack_kernel(const uint16_t* __restrict__ v, uint16_t* __restrict__ vt,
+                                                    int64_t nk, int heads, int64_t ntile, Tiling tg) {
+  constexpr int DC = D / 8;  // 8-column chunks of a row
+  const int64_t blk = blockIdx.x;  // (b * heads + h) * ntile + tile
+  const int64_t tile = blk % ntile, bh = blk / ntile;
+  const int h = (int)(bh % heads);
+  const int64_t b = bh / heads;
+  const int dc = threadIdx.x % DC, kg = threadIdx.x / DC;
+  u32x4 in[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t key = tile * kBN + kg * 8 + j;
+    const int64_t row = TL && key < nk ? (int64_t)raster_row(tg, (int)key) : key;
+    in[j] = key < nk ? *(const u32x4*)(v + ((b * nk + row) * heads + h) * D + dc * 8) : u32x4{0, 0, 0, 0};
+  }
+  uint16_t* out = vt + blk * (int64_t)(D * kBN) + (int64_t)(dc * 8) * kBN + kg * 8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {  // head-dim row dc 8 + i: keys kg 8 .. kg 8 + 7
+    u32x4 r;
+#pragma unroll
+    for (int q2 = 0; q2 < 4; ++q2) {
+      const uint32_t lo = in[2 * q2][i / 2], hi = in[2 * q2 + 1][i / 2];
+      r[q2] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+    }
+    *(u32x4*)(out + (int64_t)i * kBN) = r;
   }
 }
 
@@ -752,6 +831,8 @@ struct FwdPlan {
   size_t ws_bytes;
   int tw = 1;      // stream tiles per LDS stage
   int splits = 1;  // chunks per row's key stream (split_merge_kernel adds them)
+  bool vt = false;     // V packed transposed (vt_pack_kernel) into the workspace at vt_off
+  size_t vt_off = 0;
 };
 
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -825,6 +906,30 @@ FwdPlan plan_fwd(const AttnArgs& a, bool have_ws) {
   return p;
 }
 
+// Bytes of the packed V^T when a call can use it, else 0: key blocks of a multiple of 64
+// (tiles start at multiples of 64, in tile-major order when tiled), and at least as many
+// queries as keys, so that each key tile is read by many query blocks and one packing pass
+// over V pays off.
+size_t vt_bytes(const AttnArgs& a) {
+  if (a.block_k % kBN != 0 || a.nq < a.nk) return 0;
+  return align256(2 * (size_t)(a.batch * a.heads) * (size_t)((a.nk + kBN - 1) / kBN) * kBN * (size_t)a.head_dim);
+}
+
+// The plan for `have` workspace bytes: the grouped / split plan when its lists and partials
+// fit, then the packed V^T after them when it fits too.
+FwdPlan plan_fwd_ws(const AttnArgs& a, size_t have) {
+  const bool core = have >= plan_fwd(a, true).ws_bytes;
+  FwdPlan p = plan_fwd(a, core);
+  if (!core) p.ws_bytes = 0;  // neither grouped nor split: no bytes of the workspace used yet
+  const size_t vb = vt_bytes(a);
+  if (vb && have >= p.ws_bytes && have - p.ws_bytes >= vb) {
+    p.vt = true;
+    p.vt_off = p.ws_bytes;
+    p.ws_bytes += vb;
+  }
+  return p;
+}
+
 // Kernel view of the tile grid (a.tiled) and its copy mode; all zero when not tiled.
 Tiling make_tiling(const AttnArgs& a) {
   Tiling t{};
@@ -881,7 +986,8 @@ int tiling_mode(int th, int tw) {
   return 0;
 }
 
-size_t attn_fwd_workspace(const AttnArgs& a) { return plan_fwd(a, true).ws_bytes; }
+size_t attn_fwd_workspace(const AttnArgs& a) { return plan_fwd_ws(a, SIZE_MAX).ws_bytes; }
+size_t attn_fwd_workspace_min(const AttnArgs& a) { return plan_fwd(a, true).ws_bytes; }
 
 hipError_t launch_attn_fwd(const AttnArgs& a, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const int nbq = (int)((a.nq + a.block_q - 1) / a.block_q);
@@ -904,7 +1010,19 @@ hipError_t launch_attn_fwd(const AttnArgs& a, void* workspace, size_t workspace_
     return hipGetLastError();
   }
   const float sl2 = a.scale * kLog2e;
-  const FwdPlan pl = plan_fwd(a, workspace != nullptr && workspace_bytes >= plan_fwd(a, true).ws_bytes);
+  const FwdPlan pl = plan_fwd_ws(a, workspace != nullptr ? workspace_bytes : 0);
+  const uint16_t* vsrc = (const uint16_t*)a.v;
+  if (pl.vt) {
+    uint16_t* vt = (uint16_t*)((char*)workspace + pl.vt_off);
+    const int64_t ntile = (a.nk + kBN - 1) / kBN;
+    auto pack = a.head_dim == 64 ? (a.tiled ? vt_pack_kernel<64, true> : vt_pack_kernel<64, false>)
+                                 : (a.tiled ? vt_pack_kernel<128, true> : vt_pack_kernel<128, false>);
+    hipLaunchKernelGGL(pack, dim3((unsigned)(a.batch * a.heads * ntile)), dim3(a.head_dim), 0, stream,
+                       (const uint16_t*)a.v, vt, a.nk, a.heads, ntile, tg);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    vsrc = vt;
+  }
   Work wk;
   Groups gp{1, 1, 0, 1};
   const int32_t *kcol = a.col_idx, *gmask = nullptr, *gcnt = nullptr;
@@ -943,45 +1061,46 @@ hipError_t launch_attn_fwd(const AttnArgs& a, void* workspace, size_t workspace_
   const dim3 grid((unsigned)(wk.per_xcd * 8));
   auto launch = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(pl.nw * kWave), 0, stream, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.nq, a.nk,
+                       (const uint16_t*)a.k, vsrc, (uint16_t*)a.o, a.lse, a.nq, a.nk,
                        a.heads, a.block_q, a.block_k, a.row_ptr, kcol, gmask, gcnt, a.n_slabs, sl2, wk, gp, tg, sp);
   };
-  // instantiation for (head_dim, plan, tiled)
-  auto pick = [&](auto dc, auto tc) {
+  // instantiation for (head_dim, plan, tiled, packed V^T)
+  auto pick = [&](auto dc, auto tc, auto vc) {
     constexpr int D = decltype(dc)::value;
     constexpr bool TL = decltype(tc)::value;
+    constexpr bool VT = decltype(vc)::value;
     if (pl.grouped) {
       if constexpr (!TL) {
-        if (pl.tw == 2 && pl.nw == 12) return launch(attn_fwd_bf16_kernel<D, 1, 12, true, false, 2, false>);
-        if (pl.tw == 2) return launch(attn_fwd_bf16_kernel<D, 1, 8, true, false, 2, false>);
+        if (pl.tw == 2 && pl.nw == 12) return launch(attn_fwd_bf16_kernel<D, 1, 12, true, false, 2, false, VT>);
+        if (pl.tw == 2) return launch(attn_fwd_bf16_kernel<D, 1, 8, true, false, 2, false, VT>);
       }
-      if (pl.nw == 12) launch(attn_fwd_bf16_kernel<D, 1, 12, true, TL, 1, false>);
-      else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<D, 1, 8, true, TL, 1, false>);
-      else launch(attn_fwd_bf16_kernel<D, 1, 4, true, TL, 1, false>);
+      if (pl.nw == 12) launch(attn_fwd_bf16_kernel<D, 1, 12, true, TL, 1, false, VT>);
+      else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<D, 1, 8, true, TL, 1, false, VT>);
+      else launch(attn_fwd_bf16_kernel<D, 1, 4, true, TL, 1, false, VT>);
       return;
     }
     if (pl.splits > 1) {
-      if (pl.ks == 2) launch(attn_fwd_bf16_kernel<D, 2, 4, false, TL, 1, true>);
-      else if (pl.nw == 12) launch(attn_fwd_bf16_kernel<D, 1, 12, false, TL, 1, true>);
-      else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<D, 1, 8, false, TL, 1, true>);
-      else launch(attn_fwd_bf16_kernel<D, 1, 4, false, TL, 1, true>);
+      if (pl.ks == 2) launch(attn_fwd_bf16_kernel<D, 2, 4, false, TL, 1, true, VT>);
+      else if (pl.nw == 12) launch(attn_fwd_bf16_kernel<D, 1, 12, false, TL, 1, true, VT>);
+      else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<D, 1, 8, false, TL, 1, true, VT>);
+      else launch(attn_fwd_bf16_kernel<D, 1, 4, false, TL, 1, true, VT>);
       return;
     }
-    if (pl.ks == 2) launch(attn_fwd_bf16_kernel<D, 2, 4, false, TL, 1, false>);
-    else if (pl.nw == 12) launch(attn_fwd_bf16_kernel<D, 1, 12, false, TL, 1, false>);
-    else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<D, 1, 8, false, TL, 1, false>);
-    else launch(attn_fwd_bf16_kernel<D, 1, 4, false, TL, 1, false>);
+    if (pl.ks == 2) launch(attn_fwd_bf16_kernel<D, 2, 4, false, TL, 1, false, VT>);
+    else if (pl.nw == 12) launch(attn_fwd_bf16_kernel<D, 1, 12, false, TL, 1, false, VT>);
+    else if (pl.nw == 8) launch(attn_fwd_bf16_kernel<D, 1, 8, false, TL, 1, false, VT>);
+    else launch(attn_fwd_bf16_kernel<D, 1, 4, false, TL, 1, false, VT>);
   };
   using D64 = std::integral_constant<int, 64>;
   using D128 = std::integral_constant<int, 128>;
   using Yes = std::integral_constant<bool, true>;
   using No = std::integral_constant<bool, false>;
   if (a.head_dim == 64) {
-    if (a.tiled) pick(D64{}, Yes{});
-    else pick(D64{}, No{});
+    if (a.tiled) pl.vt ? pick(D64{}, Yes{}, Yes{}) : pick(D64{}, Yes{}, No{});
+    else pl.vt ? pick(D64{}, No{}, Yes{}) : pick(D64{}, No{}, No{});
   } else {
-    if (a.tiled) pick(D128{}, Yes{});
-    else pick(D128{}, No{});
+    if (a.tiled) pl.vt ? pick(D128{}, Yes{}, Yes{}) : pick(D128{}, Yes{}, No{});
+    else pl.vt ? pick(D128{}, No{}, Yes{}) : pick(D128{}, No{}, No{});
   }
   if (pl.splits > 1) {
     const hipError_t e = hipGetLastError();

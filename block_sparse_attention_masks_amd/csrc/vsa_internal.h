@@ -131,7 +131,10 @@ constexpr int kTiledMaxCopyTiles = 64;
 int64_t tiling_lane_span(int H, int W, int th, int tw);
 // Workspace the bf16 forward uses for grouped query blocks (0 if none); without it the
 // call runs ungrouped.
+// Workspace bytes of the fastest plan (union lists, split partials, packed V^T), and the
+// least with which the call still runs grouped / split as planned (no packed V^T).
 size_t attn_fwd_workspace(const AttnArgs& a);
+size_t attn_fwd_workspace_min(const AttnArgs& a);
 hipError_t launch_attn_fwd(const AttnArgs& a, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 struct AttnBwdArgs {

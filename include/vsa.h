@@ -320,12 +320,18 @@ vsa_status vsa_mask_nabla(const void* q, const void* k, int32_t dtype,
  * kept-block list is instead cut into up to 8 contiguous chunks walked by separate workgroups, whose
  * fp32 partial outputs (with their running maximum and row sum) a second kernel
  * adds in chunk order: the result is deterministic and equals the unsplit run to
- * rounding.  The workspace (device, 256-byte aligned) holds the union lists or the
- * partial outputs; with workspace = NULL, or smaller than the query, the call runs
- * neither grouped nor split.  Grouped and ungrouped runs give the same result bit for
- * bit for query blocks of 65 to 128 rows; ungrouped blocks of at most 64 rows split
- * each key tile between two waves and add their halves at the end, so there the two
- * agree to rounding only.
+ * rounding.  Third, when key blocks are a multiple of 64 tokens and nq >= nk (every
+ * key tile is then read by many query blocks), V is first copied transposed into the
+ * workspace, [batch, heads, ceil(nk / 64), head_dim, 64], so the P V product reads it
+ * 16 bytes per lane.  The workspace (device, 256-byte aligned) holds, in this order,
+ * the union lists or the partial outputs, then the transposed V; the size query
+ * reports all of it.  A smaller workspace is used as far as it goes: the transposed V
+ * only if it fits after the lists or partials, and with workspace = NULL, or smaller
+ * than the lists or partials, the call runs neither grouped nor split.  Runs with the
+ * same V layout and tile walk give the same result bit for bit (grouped and ungrouped
+ * query blocks of 65 to 128 rows); the transposed V and the two-wave split of each key
+ * tile for ungrouped blocks of at most 64 rows change the summation order, so across
+ * those the results agree to rounding only.
  * bf16 token rows must be below 2^24 bytes (heads * head_dim * 2 < 2^24, i.e. at most
  * 65,535 heads at head_dim 128); the kernels address a tile's rows in 24-bit arithmetic.
  * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE, VSA_ERR_DTYPE, VSA_ERR_PARAM (n_slabs, scale),
@@ -348,17 +354,18 @@ vsa_status vsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v
  * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
  *
  * The workspace the forward would ask for (union lists of grouped query blocks, or
- * the partial outputs of split key streams) is taken from a 64 MiB array that the
- * library holds on every GPU it runs on until the process ends; every other argument
- * and the result are those of vsa_block_sparse_attn_fwd with a workspace.  The array
+ * the partial outputs of split key streams, then the transposed V when it fits in
+ * what is left) is taken from a 64 MiB array that the library holds on every GPU it
+ * runs on until the process ends; every other argument and the result are those of
+ * vsa_block_sparse_attn_fwd with a workspace of that size.  The array
  * is state shared by every call on a GPU: calls that overlap on one GPU (two streams,
  * or two threads) race and must be serialised by the caller.  Nothing in it needs to
  * start at zero (every value is written before it is read), and it keeps the last
  * call's contents.  The call allocates nothing: no hipMalloc, hipFree or allocating
  * library routine.
  * Errors: as for vsa_block_sparse_attn_fwd; VSA_ERR_CAPACITY (checked before anything
- * touches the device) when the problem needs more than 64 MiB of workspace (query it
- * with vsa_block_sparse_attn_fwd and workspace = NULL).
+ * touches the device) when the union lists or partial outputs alone need more than
+ * 64 MiB (the transposed V is optional and skipped when it does not fit).
  */
 vsa_status vsa_block_sparse_attn_fwd_static(const void* q, const void* k, const void* v, void* o,
                                             float* lse, int32_t dtype, int64_t batch, int32_t heads,
@@ -411,8 +418,10 @@ vsa_status vsa_radial_attn_fwd(const void* q, const void* k, const void* v, void
  *             order.
  * row_ptr/col_idx  CSR over the tile-major tiles (n_tiles = T/tt * H/th * W/tw rows
  *             per slab; vsa_mask_sta's output), n_slabs = 1 or batch*heads.
- * workspace / workspace_bytes, scale: as for vsa_block_sparse_attn_fwd (grouping and the
- * split of small problems included).
+ * workspace / workspace_bytes, scale: as for vsa_block_sparse_attn_fwd (grouping, the
+ * split of small problems and the transposed V included; here the transposed copy is
+ * in tile-major key order).  The bit-for-bit equality above holds between calls given
+ * the workspace each one asks for, or none.
  * The tile's h-w plane must nest with the kernel's 64-token copy tile: th*tw a
  * multiple of 64 with tw dividing 64 or a multiple of 64, or th*tw dividing 64 (the
  * 6x8x8 and 1x8x8 tiles of the pages' video models qualify), and a tile holds at

@@ -139,7 +139,11 @@ def test_attn_validation(L):
     assert attn(L, scale=float("nan"))[0] == E_PARAM
     assert attn(L, scale=-0.1)[0] == E_PARAM
     assert attn(L, o=ODD)[0] == E_UNSUP
-    assert attn(L, query=True) == (OK, 0)
+    # the size query reports the packed V^T (2 heads x 2 tiles of 64 keys x 128 x 2 bytes) ...
+    assert attn(L, query=True) == (OK, 65536)
+    # ... which fewer queries than keys, or key blocks that are not a multiple of 64, do not use
+    assert attn(L, nq=99, query=True) == (OK, 0)
+    assert attn(L, bk=96, query=True) == (OK, 0)
     # bf16 token rows of 2^24 bytes or more: the kernels' 24-bit row offsets would wrap
     assert attn(L, H=65536, D=128)[0] == E_UNSUP
     assert attn(L, H=65536, D=128, query=True)[0] == E_UNSUP
@@ -197,7 +201,8 @@ def test_tiled_attn_validation(L):
     assert tiled(L, grid=(64, 256, 256), tile=(1, 1, 1), H=1, D=64, query=True)[0] == OK
     assert tiled(L, grid=(64, 1024, 1024), tile=(1, 1, 1), H=1, D=64, dtype=0, query=True)[0] == OK  # fp32 path
     # workspace: none for 384-token tiles, the union lists for 64-token tiles (grouped)
-    assert tiled(L, query=True) == (OK, 0)
+    # the packed V^T: 12 x 16 x 16 tokens = 48 tiles of 64 keys, 2 heads, 128 x 2 bytes each
+    assert tiled(L, query=True) == (OK, 48 * 2 * 64 * 128 * 2)
     assert tiled(L, grid=(12, 64, 64), tile=(1, 8, 8), query=True)[1] > 0
 
 

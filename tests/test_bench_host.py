@@ -52,14 +52,14 @@ def test_attn_flops_dense_closed_form():
 
 
 @pytest.mark.parametrize("profile,args", [
-    ("path_sta_kernel_stats.md", dict(D=128, block_q=384, block_k=384, grouped=False, heads=24,
-                                      n_qblocks=300, tiled=True)),
+    ("path_sta_kernel_stats.md", dict(D=128, block_q=384, block_k=384, grouped=True, heads=24,
+                                      n_qblocks=300, tiled=True, nq=115200, nk=115200)),
     ("path_nabla_kernel_stats.md", dict(D=128, block_q=64, block_k=64, grouped=True, heads=40,
-                                        n_qblocks=960)),
+                                        n_qblocks=960, nq=61440, nk=61440)),
     ("path_radial_kernel_stats.md", dict(D=128, block_q=128, block_k=128, grouped=True, heads=24,
-                                         n_qblocks=3516)),
+                                         n_qblocks=3516, nq=450000, nk=450000)),
     ("path_ar_kernel_stats.md", dict(D=128, block_q=64, block_k=64, grouped=True, heads=12,
-                                     n_qblocks=74, n_kblocks=512)),
+                                     n_qblocks=74, n_kblocks=512, nq=4680, nk=32760)),
 ])
 def test_kernel_label_is_the_profiled_kernel(profile, args):
     """The label the bench line divides by must name the kernel the trace of that
