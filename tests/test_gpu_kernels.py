@@ -177,6 +177,51 @@ def test_attention_parity(case):
     _check(o, lse, o_ref, lse_ref, dtype)
 
 
+@pytest.mark.parametrize("B,H,D,nq,nk,bq,bk", [
+    (2, 3, 128, 900, 830, 384, 384),   # 12-wave blocks, ragged last key tile
+    (2, 3, 64, 900, 830, 64, 64),      # 4-wave key split (KS = 2), head_dim 64
+])
+def test_packed_v_transpose(B, H, D, nq, nk, bq, bk):
+    """A call that neither groups nor splits uses its workspace for V^T alone: after the call it
+    holds V as [batch, heads, 64-key tile, head_dim, 64], keys past nk zero, bit for bit.  The
+    output matches the oracle and equals the row-major-V run (no workspace) to rounding."""
+    slabs = B * H
+    scale = D ** -0.5
+    q, k, v = rand((B, nq, H, D), torch.bfloat16, 60), rand((B, nk, H, D), torch.bfloat16, 61), \
+        rand((B, nk, H, D), torch.bfloat16, 62)
+    nbq, nbk = -(-nq // bq), -(-nk // bk)
+    rng = np.random.default_rng(63)
+    keep = rng.random((slabs * nbq, nbk)) < 0.6
+    keep[np.arange(slabs * nbq), rng.integers(0, nbk, size=slabs * nbq)] = True
+    keep[:, -1] = True                                            # the ragged last key block
+    rp, ci = oracle.csr_from_bool(keep)
+    rpd, cid = torch.from_numpy(rp).to(DEV), torch.from_numpy(ci).to(DEV)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    ntile = -(-nk // 64)
+    vt_bytes = 2 * B * H * ntile * 64 * D
+    assert vsa.attn_fwd_workspace_bytes(qd, kd, rpd, cid, bq, bk, slabs) == vt_bytes   # V^T only
+    ws = torch.full((vt_bytes,), 0xff, dtype=torch.uint8, device=DEV)
+    o, lse = vsa.vsa_block_sparse_attn_fwd(qd, kd, vd, rpd, cid, bq, bk, slabs, scale, workspace=ws)
+    torch.cuda.synchronize()
+    want = torch.zeros((B, ntile * 64, H, D), dtype=torch.bfloat16)
+    want[:, :nk] = v
+    want = want.view(B, ntile, 64, H, D).permute(0, 3, 1, 4, 2).contiguous()   # [B, H, tile, D, 64]
+    got = ws.view(torch.bfloat16).view(B, H, ntile, D, 64).cpu()
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+    o_row, _ = vsa.vsa_block_sparse_attn_fwd(qd, kd, vd, rpd, cid, bq, bk, slabs, scale, grouped=False)
+    assert (o.float() - o_row.float()).abs().max() <= BF16_MAX
+    errs = []
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        rows = np.concatenate([np.arange(0, 64), rng.choice(nq, 64, replace=False), [nq - 1]])
+        base = (b * H + h) * nbq
+        ref, ref_lse = oracle.attention_rows(to_np(q[b, rows, h]), rows, to_np(k[b, :, h]), to_np(v[b, :, h]),
+                                             rp, ci, base, bq, bk, scale)
+        errs.append(np.abs(o[b, rows, h].cpu().double().numpy() - ref))
+        assert np.abs(lse[b, h, rows].cpu().double().numpy() - ref_lse).max() < 2e-2
+    err = np.concatenate(errs)
+    assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN
+
+
 def test_attention_deterministic_and_dense_mask():
     q, k, v = (rand((1, 1500, 2, 128), torch.bfloat16, s).to(DEV) for s in (20, 21, 22))
     rp, ci = vsa.all_ones_mask(-(-1500 // 128), -(-1500 // 128), DEV)
