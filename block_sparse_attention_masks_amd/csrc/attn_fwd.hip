@@ -912,6 +912,8 @@ FwdPlan plan_fwd(const AttnArgs& a, bool have_ws) {
 // over V pays off.
 size_t vt_bytes(const AttnArgs& a) {
   if (a.block_k % kBN != 0 || a.nq < a.nk) return 0;
+  // the packing kernel's grid: one workgroup per (batch, head, tile), at most 2^31 - 1
+  if (a.batch * a.heads * ((a.nk + kBN - 1) / kBN) > (int64_t)INT32_MAX) return 0;
   return align256(2 * (size_t)(a.batch * a.heads) * (size_t)((a.nk + kBN - 1) / kBN) * kBN * (size_t)a.head_dim);
 }
 
