@@ -700,35 +700,48 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
 
 // V^T packing for the VT forward: v [batch, nk, heads, D] -> vt [batch, heads, ceil(nk / 64),
 // D, 64], keys past nk zero; tiled (TL), key p of the packed order is raster row
-// raster_row(p), so the copy is in tile-major order.  Workgroup = one (batch, head, 64-key
-// tile); thread = 8 keys x 8 head-dim columns (16-byte loads of 8 key rows, an 8 x 8 transpose
-// in registers, 16-byte stores of 8 head-dim rows).  One HBM read and one write of V.
+// raster_row(p), so the copy is in tile-major order.  Workgroup = one (batch, 64-key tile), all
+// heads, so it streams whole token rows; thread = 8 keys x 8 head-dim columns of one head
+// (16-byte loads of 8 key rows, an 8 x 8 transpose in registers, 16-byte stores of 8 head-dim
+// rows), kPackThreads / D heads at a time.  One HBM read and one write of V.
+constexpr int kPackThreads = 256;
 template <int D, bool TL>
-__global__ __launch_bounds__(D) void vt_pack_kernel(const uint16_t* __restrict__ v, uint16_t* __restrict__ vt,
-                                                    int64_t nk, int heads, int64_t ntile, Tiling tg) {
-  constexpr int DC = D / 8;  // 8-column chunks of a row
-  const int64_t blk = blockIdx.x;  // (b * heads + h) * ntile + tile
-  const int64_t tile = blk % ntile, bh = blk / ntile;
-  const int h = (int)(bh % heads);
-  const int64_t b = bh / heads;
-  const int dc = threadIdx.x % DC, kg = threadIdx.x / DC;
-  u32x4 in[8];
+__global__ __launch_bounds__(kPackThreads) void vt_pack_kernel(const uint16_t* __restrict__ v,
+                                                               uint16_t* __restrict__ vt, int64_t nk, int heads,
+                                                               int64_t ntile, Tiling tg) {
+  constexpr int DC = D / 8;                // 8-column chunks of a row
+  constexpr int HP = kPackThreads / D;     // heads per pass
+  const int64_t tile = blockIdx.x % ntile, b = blockIdx.x / ntile;
+  const int t = threadIdx.x % D, hsub = threadIdx.x / D;
+  const int dc = t % DC, kg = t / DC;
+  // tiled: the 8 keys start at a multiple of 8, so when tw is a multiple of 8 they are 8
+  // consecutive tokens of one raster row of the tile, and one raster_row serves all of them
+  const int64_t key0 = tile * kBN + kg * 8;
+  const bool run8 = TL && tg.tw % 8 == 0;
+  const int64_t row0 = run8 && key0 < nk ? (int64_t)raster_row(tg, (int)key0) : key0;
+  int64_t row[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int64_t key = tile * kBN + kg * 8 + j;
-    const int64_t row = TL && key < nk ? (int64_t)raster_row(tg, (int)key) : key;
-    in[j] = key < nk ? *(const u32x4*)(v + ((b * nk + row) * heads + h) * D + dc * 8) : u32x4{0, 0, 0, 0};
+    const int64_t key = key0 + j;
+    row[j] = !TL ? key : (run8 ? row0 + j : (key < nk ? (int64_t)raster_row(tg, (int)key) : key));
   }
-  uint16_t* out = vt + blk * (int64_t)(D * kBN) + (int64_t)(dc * 8) * kBN + kg * 8;
+  for (int h = hsub; h < heads; h += HP) {
+    u32x4 in[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {  // head-dim row dc 8 + i: keys kg 8 .. kg 8 + 7
-    u32x4 r;
+    for (int j = 0; j < 8; ++j)
+      in[j] = key0 + j < nk ? *(const u32x4*)(v + ((b * nk + row[j]) * heads + h) * D + dc * 8)
+                            : u32x4{0, 0, 0, 0};
+    uint16_t* out = vt + ((b * heads + h) * ntile + tile) * (int64_t)(D * kBN) + (int64_t)(dc * 8) * kBN + kg * 8;
 #pragma unroll
-    for (int q2 = 0; q2 < 4; ++q2) {
-      const uint32_t lo = in[2 * q2][i / 2], hi = in[2 * q2 + 1][i / 2];
-      r[q2] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+    for (int i = 0; i < 8; ++i) {  // head-dim row dc 8 + i: keys kg 8 .. kg 8 + 7
+      u32x4 r;
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        const uint32_t lo = in[2 * q2][i / 2], hi = in[2 * q2 + 1][i / 2];
+        r[q2] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+      }
+      *(u32x4*)(out + (int64_t)i * kBN) = r;
     }
-    *(u32x4*)(out + (int64_t)i * kBN) = r;
   }
 }
 
@@ -912,8 +925,8 @@ FwdPlan plan_fwd(const AttnArgs& a, bool have_ws) {
 // over V pays off.
 size_t vt_bytes(const AttnArgs& a) {
   if (a.block_k % kBN != 0 || a.nq < a.nk) return 0;
-  // the packing kernel's grid: one workgroup per (batch, head, tile), at most 2^31 - 1
-  if (a.batch * a.heads * ((a.nk + kBN - 1) / kBN) > (int64_t)INT32_MAX) return 0;
+  // the packing kernel's grid: one workgroup per (batch, tile), at most 2^31 - 1
+  if (a.batch * ((a.nk + kBN - 1) / kBN) > (int64_t)INT32_MAX) return 0;
   return align256(2 * (size_t)(a.batch * a.heads) * (size_t)((a.nk + kBN - 1) / kBN) * kBN * (size_t)a.head_dim);
 }
 
@@ -1019,7 +1032,7 @@ hipError_t launch_attn_fwd(const AttnArgs& a, void* workspace, size_t workspace_
     const int64_t ntile = (a.nk + kBN - 1) / kBN;
     auto pack = a.head_dim == 64 ? (a.tiled ? vt_pack_kernel<64, true> : vt_pack_kernel<64, false>)
                                  : (a.tiled ? vt_pack_kernel<128, true> : vt_pack_kernel<128, false>);
-    hipLaunchKernelGGL(pack, dim3((unsigned)(a.batch * a.heads * ntile)), dim3(a.head_dim), 0, stream,
+    hipLaunchKernelGGL(pack, dim3((unsigned)(a.batch * ntile)), dim3(kPackThreads), 0, stream,
                        (const uint16_t*)a.v, vt, a.nk, a.heads, ntile, tg);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

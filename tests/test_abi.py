@@ -144,8 +144,10 @@ def test_attn_validation(L):
     # ... which fewer queries than keys, or key blocks that are not a multiple of 64, do not use
     assert attn(L, nq=99, query=True) == (OK, 0)
     assert attn(L, bk=96, query=True) == (OK, 0)
-    # ... or whose packing grid (one workgroup per batch x head x 64-key tile) would pass 2^31 - 1
-    assert attn(L, H=65535, nq=2 ** 30, nk=2 ** 30, bq=2 ** 20, bk=2 ** 20, query=True) == (OK, 0)
+    # ... or whose packing grid (one workgroup per batch entry x 64-key tile) would pass 2^31 - 1
+    assert attn(L, B=128, H=1, nq=2 ** 30, nk=2 ** 30, bq=2 ** 20, bk=2 ** 20, query=True) == (OK, 0)
+    assert attn(L, B=127, H=1, nq=2 ** 30, nk=2 ** 30, bq=2 ** 20, bk=2 ** 20, query=True) == \
+        (OK, 2 * 127 * 2 ** 24 * 64 * 128)
     # bf16 token rows of 2^24 bytes or more: the kernels' 24-bit row offsets would wrap
     assert attn(L, H=65536, D=128)[0] == E_UNSUP
     assert attn(L, H=65536, D=128, query=True)[0] == E_UNSUP
