@@ -646,7 +646,7 @@ def main():
                ratio_to_attn=round(med / attn_ms, 5))
     pool_out = torch.empty((path.B, path.H, path.nbk, path.D), dtype=torch.float64, device=dev)
     med, mn = time_hbm_pass(lambda: path.vsa.vsa_block_mean_pool(path.ka, path.bk, out=pool_out), stream, flush)
-    pool = hbm(med, mn, k_bytes, kernel=f"pool_kernel<true, {8 if path.bk >= 128 else 4}>",
+    pool = hbm(med, mn, k_bytes, kernel="pool_kernel<true>",
                tensor="K in attention order", block=path.bk,
                bytes_written=pool_out.numel() * 8,
                gbs_with_writes=round((k_bytes + pool_out.numel() * 8) / (med * 1e-3) / 1e9, 1))

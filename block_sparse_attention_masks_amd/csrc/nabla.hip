@@ -80,17 +80,17 @@ struct Vec8 {
 // grid: x = (block, 64-vector slice of a row) with the slice fastest (a vector = 8
 // elements; blocks are the query blocks, then the key blocks), z = batch: the workgroups
 // that run side by side read neighbouring parts of the same rows, so whole rows stream
-// from each DRAM page.  The kPoolWaves waves of a workgroup split the block's valid rows
-// into contiguous parts; lane l of every wave sums vector 64 y + l of its rows, keeping U
-// rows' loads in flight, and the parts meet in LDS.  Splitting the rows makes the waves
-// short and many (one wave per row part rather than per block), so the last round of waves
-// on the chip is a small share of the pass.  The sums of bf16 values are exact in fp64,
-// so the order in which the parts are added does not matter.  The element type and the
-// number of waves are template parameters so that each kernel holds only its own registers:
-// 8 waves with 16 rows in flight per lane for blocks of >= 128 rows, 4 waves with 8 rows in
-// flight for smaller blocks (measured with the caches flushed: 71.4% against 68.7% of HBM on
-// 128-row blocks, 67.3% against 66.2% on 64-row blocks; 384-row blocks ~75% either way).
-template <bool BF16, int kPoolWaves>
+// from each DRAM page.  The kPoolWaves waves of a workgroup interleave over the block's valid
+// rows (wave w takes rows w, w + 8, ...), so a workgroup sweeps consecutive rows together;
+// lane l of every wave sums vector 64 y + l of its rows, keeping 64 bytes of loads in flight
+// (4 bf16 rows or 2 fp32 rows) so that a wave of even a 64-row block loads in two batches,
+// and the waves' sums meet in LDS.  The sums of bf16 values are exact in fp64, so the order
+// in which rows and waves are added does not matter.  The element type is a template
+// parameter so that each kernel holds only its own registers.  Measured with the caches
+// flushed: 68-69% of HBM on 64-row blocks (66-67% with contiguous row parts per wave and
+// one batch), 71-72% on 128-row and 74-75% on 384-row blocks, the same as before.
+constexpr int kPoolWaves = 8;
+template <bool BF16>
 __global__ __launch_bounds__(kPoolWaves * kWave) void pool_kernel(const uint8_t* __restrict__ q,
                                                            const uint8_t* __restrict__ k,
                                                            int64_t nq, int64_t nk, int bq, int bk,
@@ -114,26 +114,25 @@ __global__ __launch_bounds__(kPoolWaves * kWave) void pool_kernel(const uint8_t*
   constexpr int esz = BF16 ? 2 : 4;
   const int64_t row_bytes = (int64_t)hd * esz;
   const int64_t t0 = (int64_t)blk * bsz, t1 = min(n, t0 + bsz);
-  const int64_t per = (t1 - t0 + kPoolWaves - 1) / kPoolWaves;
-  const int64_t r0 = min(t1, t0 + w * per), r1 = min(t1, r0 + per);
+  constexpr int W = kPoolWaves;
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (active) {
-    const uint8_t* p = src + (b * n + r0) * row_bytes + (int64_t)vec * 8 * esz;
-    int64_t t = r0;
-    constexpr int U = (BF16 ? 16 : 8) / (kPoolWaves == 8 ? 1 : 2);
-    for (; t + U <= r1; t += U) {
+    const uint8_t* p = src + (b * n + t0 + w) * row_bytes + (int64_t)vec * 8 * esz;
+    int64_t t = t0 + w;
+    constexpr int U = BF16 ? 4 : 2;
+    for (; t + (U - 1) * W < t1; t += U * W) {
       Vec8<BF16> x[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) x[u].load(p + u * row_bytes);
+      for (int u = 0; u < U; ++u) x[u].load(p + u * W * row_bytes);
 #pragma unroll
       for (int u = 0; u < U; ++u) x[u].add_to(acc);
-      p += U * row_bytes;
+      p += U * W * row_bytes;
     }
-    for (; t < r1; ++t) {
+    for (; t < t1; t += W) {
       Vec8<BF16> x;
       x.load(p);
       x.add_to(acc);
-      p += row_bytes;
+      p += W * row_bytes;
     }
   }
   if (w > 0) {
@@ -158,10 +157,8 @@ hipError_t launch_pool(const void* q, const void* k, int bf16, int64_t batch, in
                        hipStream_t stream) {
   const int slices = (heads * D / 8 + kWave - 1) / kWave;
   const dim3 grid((unsigned)((nbq + nbk) * slices), 1, (unsigned)batch);
-  const bool wide = (nbk == 0 || bk >= 128) && bq >= 128;
-  auto kern = wide ? (bf16 ? pool_kernel<true, 8> : pool_kernel<false, 8>)
-                   : (bf16 ? pool_kernel<true, 4> : pool_kernel<false, 4>);
-  hipLaunchKernelGGL(kern, grid, dim3((wide ? 8 : 4) * kWave), 0, stream, (const uint8_t*)q, (const uint8_t*)k, nq,
+  auto kern = bf16 ? pool_kernel<true> : pool_kernel<false>;
+  hipLaunchKernelGGL(kern, grid, dim3(kPoolWaves * kWave), 0, stream, (const uint8_t*)q, (const uint8_t*)k, nq,
                      nk, bq, bk, nbq, nbk, heads, D, slices, qp, kp);
   return hipGetLastError();
 }

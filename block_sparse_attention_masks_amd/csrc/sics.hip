@@ -110,8 +110,10 @@ __global__ __launch_bounds__(kVecs * kPhases) void sics_kernel(const uint8_t* __
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] += v[i] * inv;
   };
-  // U rows in flight per lane
-  constexpr int U = BF16 ? 8 : 4;
+  // U rows in flight per lane: 4, so that a wave of even a 64-row block (8 rows) loads in two
+  // batches and overlaps the second with the first's arithmetic (8 in flight: 66% of HBM on
+  // 64-row blocks against 83%; 84% against 86% on 128-row blocks; 384-row blocks 74% either way)
+  constexpr int U = 4;
   const uint4 zero = {0, 0, 0, 0};
   int64_t t = t0 + phase;
   for (; t + (U - 1) * kPhases < t1; t += U * kPhases) {
