@@ -960,10 +960,9 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, void* workspace, hipStream_t st
   const Work wq = make_work(a.batch, a.heads, a.nq, a.block_q, 32 * kNW / ksq);
   Work wkv = make_work(a.batch, a.heads, a.nk, a.block_k, 32 * kNW / ksk);
   if (kg.G) {  // the union of each group's query blocks, from the CSC view
-    hipLaunchKernelGGL(group_union_kernel, dim3((unsigned)((kg.lists + kUnionWaves - 1) / kUnionWaves)),
-                       dim3(kUnionWaves * kWave), 0, stream, col_ptr, row_idx, nbk, kg.lists, kg.G, kg.n_groups, 1,
-                       nbq, gidx, gmask, gcnt);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_group_union(col_ptr, row_idx, nbk, kg.lists, kg.G, kg.n_groups, 1, nbq, gidx, gmask, gcnt,
+                                stream)) != hipSuccess)
+      return e;
     wkv.nb = kg.n_groups;
     wkv.mt_per_b = 1;
     wkv.items = a.batch * a.heads * (int64_t)kg.n_groups;

@@ -1050,10 +1050,8 @@ hipError_t launch_attn_fwd(const AttnArgs& a, void* workspace, size_t workspace_
     int32_t* gcnt_w = (int32_t*)(ws + 2 * align256(4 * (size_t)(lists * nbk)));
     gmask = gmask_w;
     gcnt = gcnt_w;
-    hipLaunchKernelGGL(group_union_kernel, dim3((unsigned)((lists + kUnionWaves - 1) / kUnionWaves)),
-                       dim3(kUnionWaves * kWave), 0, stream, a.row_ptr, a.col_idx, nbq, lists, pl.G, pl.n_groups,
-                       a.group_stride, nbk, gcol, gmask_w, gcnt_w);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch_group_union(a.row_ptr, a.col_idx, nbq, lists, pl.G, pl.n_groups, a.group_stride, nbk,
+                                            gcol, gmask_w, gcnt_w, stream);
     if (e != hipSuccess) return e;
     gp = Groups{pl.G, pl.wpb, nbk, a.group_stride};
     kcol = gcol;

@@ -382,7 +382,34 @@ GROUPED_CASES = [
     # 64-key blocks and smaller: two stream tiles per LDS stage
     (1, 48, 64, 1536, 1900, 64, 64, 0.5, True),      # 8 waves, 4 blocks per group; ragged last key block
     (2, 48, 64, 2000, 1000, 64, 32, 0.5, False),     # 12 waves, 32-key blocks (half-filled tiles)
+    (1, 48, 64, 4000, 1000, 32, 64, 0.5, True),      # 32-row blocks: 12 per group
 ]
+
+
+def test_union_lists_walk_fallback():
+    """Groups whose row bitmaps do not fit the union kernel's LDS share (3 rows of 44,000
+    one-key blocks) take the list walk instead; the grouped run still equals the ungrouped
+    one bit for bit and matches the oracle."""
+    B, H, D, nq, nk, bq, bk = 1, 32, 64, 3072, 44000, 128, 1
+    scale = D ** -0.5
+    q, k, v = rand((B, nq, H, D), torch.bfloat16, 80), rand((B, nk, H, D), torch.bfloat16, 81), \
+        rand((B, nk, H, D), torch.bfloat16, 82)
+    nbq, nbk = nq // bq, nk
+    rng = np.random.default_rng(83)
+    keep = rng.random((nbq, nbk)) < 0.005
+    keep[np.arange(nbq), rng.integers(0, nbk, size=nbq)] = True
+    rp, ci = oracle.csr_from_bool(keep)
+    rpd, cid = torch.from_numpy(rp).to(DEV), torch.from_numpy(ci).to(DEV)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    assert vsa.attn_fwd_workspace_bytes(qd, kd, rpd, cid, bq, bk, 1) > 0    # this case does group
+    o_g, l_g = vsa.vsa_block_sparse_attn_fwd(qd, kd, vd, rpd, cid, bq, bk, 1, scale)
+    o_u, l_u = vsa.vsa_block_sparse_attn_fwd(qd, kd, vd, rpd, cid, bq, bk, 1, scale, grouped=False)
+    assert torch.equal(o_g, o_u) and torch.equal(l_g, l_u)
+    rows = np.concatenate([np.arange(0, 2 * bq), rng.choice(nq, 64, replace=False), [nq - 1]])
+    ref, _ = oracle.attention_rows(to_np(q[0, rows, 5]), rows, to_np(k[0, :, 5]), to_np(v[0, :, 5]),
+                                   rp, ci, 0, bq, bk, scale)
+    err = np.abs(o_g[0, rows, 5].cpu().double().numpy() - ref)
+    assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN
 
 
 @pytest.mark.parametrize("case", GROUPED_CASES, ids=[str(i) for i in range(len(GROUPED_CASES))])
