@@ -182,10 +182,19 @@ struct Smem {
   float dl[2][kT];         // dkdv: D of the tile's queries (0 past the end)
 };
 
+// Work items to workgroups, as in the forward: XCD b % 8 takes contiguous ranges (chunk = 0)
+// or runs of chunk consecutive items (xcd_run).
 struct Work {
   int64_t items, per_xcd;
   int nb, mt_per_b;
+  int chunk = 0;
 };
+
+__device__ inline int64_t work_item(const Work& wk, int64_t bid) {
+  if (wk.chunk == 0) return (bid % 8) * wk.per_xcd + bid / 8;
+  const int64_t c8 = 8 * (int64_t)wk.chunk, full = wk.items / c8 * c8;
+  return bid < full ? bid / c8 * c8 + (bid % 8) * wk.chunk + bid / 8 % wk.chunk : bid;
+}
 
 // Grouped key blocks (dK, dV with blocks of <= 64 keys): G consecutive key blocks of a
 // slab share a 4-wave workgroup (wpb waves each) and walk the union of the query blocks
@@ -397,7 +406,7 @@ __global__ __launch_bounds__(kNW * kWave, 2) void dq_kernel(
   constexpr int BM = 32 * kNW / KS;
   constexpr int NST = 2 / KS;
   const int64_t bid = blockIdx.x;
-  const int64_t item = (bid % 8) * wk.per_xcd + bid / 8;
+  const int64_t item = work_item(wk, bid);
   if (item >= wk.items) return;
   const int mt = (int)(item % wk.mt_per_b);
   int64_t rest = item / wk.mt_per_b;
@@ -549,7 +558,7 @@ __global__ __launch_bounds__(kNW * kWave, 2) void dkdv_kernel(
   constexpr int BN = 32 * kNW / KS;
   constexpr int NQS = 2 / KS;  // 32-query steps of a tile per wave
   const int64_t bid = blockIdx.x;
-  const int64_t item = (bid % 8) * wk.per_xcd + bid / 8;
+  const int64_t item = work_item(wk, bid);
   if (item >= wk.items) return;
   const int mt = (int)(item % wk.mt_per_b);
   int64_t rest = item / wk.mt_per_b;
@@ -957,8 +966,9 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, void* workspace, hipStream_t st
 
   const float sl2 = a.scale * kLog2e;
   const int ksq = a.block_q <= 64 ? 2 : 1, ksk = a.block_k <= 64 ? 2 : 1;
-  const Work wq = make_work(a.batch, a.heads, a.nq, a.block_q, 32 * kNW / ksq);
+  Work wq = make_work(a.batch, a.heads, a.nq, a.block_q, 32 * kNW / ksq);
   Work wkv = make_work(a.batch, a.heads, a.nk, a.block_k, 32 * kNW / ksk);
+  wq.chunk = wkv.chunk = xcd_run(a.nk, a.head_dim, 2);
   if (kg.G) {  // the union of each group's query blocks, from the CSC view
     if ((e = launch_group_union(col_ptr, row_idx, nbk, kg.lists, kg.G, kg.n_groups, 1, nbq, gidx, gmask, gcnt,
                                 stream)) != hipSuccess)

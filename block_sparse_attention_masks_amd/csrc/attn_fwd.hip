@@ -74,9 +74,15 @@ constexpr int kBN = 64;       // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale slack (exponents stay <= 2^8)
 
+// Work items to workgroups.  The dispatcher deals workgroup b to XCD b % 8.  chunk = 0: XCD x
+// takes the contiguous range x per_xcd .. (x + 1) per_xcd - 1.  chunk = C (xcd_run): the items
+// are cut into runs of 8 C and XCD x takes the x-th C of each run (the last, partial run keeps
+// the dispatcher's order), so the 8 XCDs work on neighbouring items of one head, whose K and V
+// they then share through the Infinity Cache, while each keeps C consecutive items for its L2.
 struct Work {
   int64_t items, per_xcd;
   int nbq, mt_per_qb;
+  int chunk = 0;
 };
 
 // Grouped query blocks: G consecutive query blocks of a slab share a workgroup of G * wpb
@@ -336,7 +342,13 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
   // work item: (batch, head, query block, row tile) -- or, grouped, (batch, head, group
   // of gp.G query blocks); wk.nbq counts query blocks or groups
   const int64_t bid = blockIdx.x;
-  int64_t item = (bid % 8) * wk.per_xcd + bid / 8;
+  int64_t item;
+  if (wk.chunk == 0) {
+    item = (bid % 8) * wk.per_xcd + bid / 8;
+  } else {
+    const int64_t c8 = 8 * (int64_t)wk.chunk, full = wk.items / c8 * c8;
+    item = bid < full ? bid / c8 * c8 + (bid % 8) * wk.chunk + bid / 8 % wk.chunk : bid;
+  }
   if (item >= wk.items) return;
   int chunk = 0;  // SP: the chunk of the row's key stream, innermost
   if constexpr (SP) {
@@ -1071,6 +1083,7 @@ hipError_t launch_attn_fwd(const AttnArgs& a, void* workspace, size_t workspace_
   }
   wk.items = a.batch * a.heads * (int64_t)wk.nbq * wk.mt_per_qb * pl.splits;
   wk.per_xcd = (wk.items + 7) / 8;
+  wk.chunk = xcd_run(a.nk, a.head_dim, 2);
   const dim3 grid((unsigned)(wk.per_xcd * 8));
   auto launch = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(pl.nw * kWave), 0, stream, (const uint16_t*)a.q,
