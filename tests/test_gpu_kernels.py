@@ -373,6 +373,53 @@ def test_attention_backward_parity(case):
         assert torch.all(dq[0, bq:min(2 * bq, nq), 0] == 0)
 
 
+def test_backward_large_heads_xcd_runs():
+    """Heads whose K and V take 138 MB (270,000 keys x 128 x bf16, twice) get the work order in
+    runs of 32 items per XCD, in the forward and in both backward kernels: 4,220 query-block
+    and 4,220 key-block items, so 16 whole runs of 256 and a partial last run in the natural
+    order.  Rows keep 12 random key blocks of 2,110; the ragged last key block (48 keys) is
+    kept by several rows and the ragged last query block keeps it.  dq on sampled rows (the
+    last one included) and dk, dv on sampled key blocks (the last one included) against the
+    oracle, to the small cases' bounds."""
+    N, H, D, blk, per_row = 270_000, 2, 128, 128, 12
+    scale = D ** -0.5
+    nb = -(-N // blk)
+    q, k, v, do = (rand((1, N, H, D), torch.bfloat16, s) for s in (90, 91, 92, 93))
+    rng = np.random.default_rng(94)
+    keep = np.zeros((nb, nb), bool)
+    for r in range(nb):
+        keep[r, rng.choice(nb, per_row, replace=False)] = True
+    keep[rng.choice(nb - 1, 8, replace=False), nb - 1] = True
+    keep[nb - 1, nb - 1] = True
+    rp, ci = oracle.csr_from_bool(keep)
+    rpd, cid = torch.from_numpy(rp).to(DEV), torch.from_numpy(ci).to(DEV)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = vsa.vsa_block_sparse_attn_fwd(qd, kd, vd, rpd, cid, blk, blk, 1, scale)
+    dq, dk, dv = vsa.vsa_block_sparse_attn_bwd(qd, kd, vd, o, dod, lse, rpd, cid, blk, blk, 1, scale)
+    torch.cuda.synchronize()
+    errs = {"dq": [], "dk": [], "dv": []}
+    refs = {"dq": [], "dk": [], "dv": []}
+    blocks = [(0, nb - 1), (1, int(rng.integers(nb - 1))), (1, int(rng.integers(nb - 1)))]
+    for h in range(H):
+        qh, kh, vh, dh = (t[0, :, h].double().numpy() for t in (q, k, v, do))
+        rows = np.union1d(rng.choice(N, 96, replace=False), [N - 1])
+        ref = oracle.attention_bwd_query_rows(qh[rows], rows, dh[rows], kh, vh, rp, ci, 0, blk, blk, scale)
+        errs["dq"].append(np.abs(dq[0, rows, h].cpu().double().numpy() - ref))
+        refs["dq"].append(np.abs(ref))
+        for j in [j for hh, j in blocks if hh == h]:
+            rk, rv = oracle.attention_bwd_key_block(j, qh, kh, vh, dh, rp, ci, 0, nb, blk, blk, scale)
+            sl = slice(j * blk, min((j + 1) * blk, N))
+            errs["dk"].append(np.abs(dk[0, sl, h].cpu().double().numpy() - rk))
+            errs["dv"].append(np.abs(dv[0, sl, h].cpu().double().numpy() - rv))
+            refs["dk"].append(np.abs(rk))
+            refs["dv"].append(np.abs(rv))
+    for name in ("dq", "dk", "dv"):
+        e, r = np.concatenate(errs[name]), np.concatenate(refs[name])
+        mx, mn = e.max() / r.max(), e.mean() / r.mean()
+        print(f"large-head bwd {name}: max_norm {mx:.2e} mean_norm {mn:.2e}", flush=True)
+        assert mx <= BWD_BF16_MAX and mn <= BWD_BF16_MEAN, name
+
+
 # ------------------------------------------------- grouped small query blocks
 GROUPED_CASES = [
     # batch, heads, D, nq, nk, bq, bk, density, per-head masks
