@@ -222,6 +222,50 @@ def test_packed_v_transpose(B, H, D, nq, nk, bq, bk):
     assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN
 
 
+@pytest.mark.parametrize("B,H,D,nq,nk,bq,bk", [
+    (1, 48, 128, 2000, 2048, 64, 64),    # the grouped plan (12 waves, 6 blocks per group)
+    (1, 2, 128, 900, 830, 384, 384),     # 12-wave blocks, packed V
+    (1, 3, 64, 500, 700, 64, 64),        # too few rows for one round: split key streams
+])
+def test_attention_mask_keeping_nothing(B, H, D, nq, nk, bq, bk):
+    """A per-head mask whose rows are all empty (the row pointers all zero, no column
+    entries): every output row is 0 with lse = -inf, and the gradients are exactly 0."""
+    slabs = B * H
+    q, k, v, do = (rand(s_, torch.bfloat16, sd).to(DEV) for s_, sd in
+                   (((B, nq, H, D), 70), ((B, nk, H, D), 71), ((B, nk, H, D), 72), ((B, nq, H, D), 73)))
+    nbq = -(-nq // bq)
+    rpd = torch.zeros(slabs * nbq + 1, dtype=torch.int32, device=DEV)
+    cid = torch.zeros(1, dtype=torch.int32, device=DEV)           # room for one entry, none used
+    o, lse = vsa.vsa_block_sparse_attn_fwd(q, k, v, rpd, cid, bq, bk, slabs, D ** -0.5)
+    dq, dk, dv = vsa.vsa_block_sparse_attn_bwd(q, k, v, o, do, lse, rpd, cid, bq, bk, slabs, D ** -0.5)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(lse == -float("inf"))
+    assert torch.all(dq == 0) and torch.all(dk == 0) and torch.all(dv == 0)
+
+
+def test_attention_one_token():
+    """One query token and one key token (one ragged block each, mostly padding): the output
+    is v itself, lse = q.k * scale, and the gradients follow from P = 1: dq = dk = 0 and
+    dv = dout (the oracle's values, to the bf16 bounds)."""
+    D = 128
+    scale = D ** -0.5
+    q, k, v, do = (rand((1, 1, 2, D), torch.bfloat16, s_) for s_ in (80, 81, 82, 83))
+    rp, ci = oracle.csr_from_bool(np.ones((2, 1), bool))
+    rpd, cid = torch.from_numpy(rp).to(DEV), torch.from_numpy(ci).to(DEV)
+    o, lse = vsa.vsa_block_sparse_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), rpd, cid, 64, 64, 2, scale)
+    dq, dk, dv = vsa.vsa_block_sparse_attn_bwd(q.to(DEV), k.to(DEV), v.to(DEV), o, do.to(DEV), lse, rpd, cid,
+                                               64, 64, 2, scale)
+    o_ref, lse_ref = oracle.attention(to_np(q), to_np(k), to_np(v), rp, ci, 64, 64, scale, 2)
+    rq, rk, rv = oracle.attention_bwd(to_np(q), to_np(k), to_np(v), to_np(do), rp, ci, 64, 64, scale, 2)
+    assert torch.equal(o.cpu(), v)                                 # softmax of one score is exactly 1
+    assert np.abs(lse.cpu().double().numpy() - lse_ref).max() < 2e-2
+    assert np.abs(dv.cpu().double().numpy() - rv).max() <= BWD_BF16_MAX * np.abs(rv).max()
+    # dq, dk: dS = P (dP - D) with dP = dout . v and D = dout . o = dout . v, the same fp32 sum (|.| ~ 10 here) taken
+    # in two orders, so what is left is its rounding (~1e-6 relative), times |k| or |q| and the scale
+    assert np.abs(dq.cpu().double().numpy()).max() <= 1e-4 and np.abs(dk.cpu().double().numpy()).max() <= 1e-4
+    assert np.abs(o_ref - to_np(v)).max() == 0 and np.abs(rq).max() < 1e-12 and np.abs(rk).max() < 1e-12
+
+
 def test_attention_deterministic_and_dense_mask():
     q, k, v = (rand((1, 1500, 2, 128), torch.bfloat16, s).to(DEV) for s in (20, 21, 22))
     rp, ci = vsa.all_ones_mask(-(-1500 // 128), -(-1500 // 128), DEV)
