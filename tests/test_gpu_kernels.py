@@ -119,6 +119,7 @@ def test_mask_nabla_bit_exact(nq, nk, bq, bk, thr, dtype):
 @pytest.mark.parametrize("nk,bk,forced,topk", [
     (3000, 64, [(0, 5), (40, 47)], 6),
     (2000, 1, [(0, 25), (1900, 2000)], 16),     # 2,000 key blocks: 8 sort slots per thread
+    (300, 64, [(0, 1)], 16),                    # fewer blocks than forced + k (5, ragged last): keep all
 ])
 def test_mask_topk_forced_bit_exact(nk, bk, forced, topk):
     q = rand((2, 700, 2, 128), torch.bfloat16, 4)
@@ -126,7 +127,7 @@ def test_mask_topk_forced_bit_exact(nk, bk, forced, topk):
     rp, ci = csr_np(*vsa.vsa_mask_nabla(q.to(DEV), k.to(DEV), 64, bk, 0.1, topk=topk, forced=forced))
     counts, _ = check_topk(rp, ci, to_np(q), to_np(k), 64, bk, 0.1, topk, forced)
     print(f"top-k mask nk {nk} block {bk}: {counts}")
-    assert set(np.diff(rp).tolist()) == {sum(hi - lo for lo, hi in forced) + topk}
+    assert set(np.diff(rp).tolist()) == {min(-(-nk // bk), sum(hi - lo for lo, hi in forced) + topk)}
 
 
 # ------------------------------------------------------------------- attention
