@@ -267,6 +267,32 @@ def test_attention_one_token():
     assert np.abs(o_ref - to_np(v)).max() == 0 and np.abs(rq).max() < 1e-12 and np.abs(rk).max() < 1e-12
 
 
+def test_attention_widest_token_rows():
+    """Token rows at the widest the bf16 kernels address (heads x head_dim x 2 bytes just below
+    2^24: 65,535 heads of 128): forward and backward on 100 tokens (a ragged second block),
+    4 sampled heads (the last included) against the oracle."""
+    H, D, N, blk = 65_535, 128, 100, 64
+    assert H * D * 2 < 1 << 24 <= (H + 1) * D * 2
+    scale = D ** -0.5
+    g = torch.Generator(device=DEV).manual_seed(95)
+    q, k, v, do = (torch.randn((1, N, H, D), generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+                   for _ in range(4))
+    keep = np.array([[True, False], [True, True]])
+    rp, ci = oracle.csr_from_bool(keep)
+    rpd, cid = torch.from_numpy(rp).to(DEV), torch.from_numpy(ci).to(DEV)
+    o, lse = vsa.vsa_block_sparse_attn_fwd(q, k, v, rpd, cid, blk, blk, 1, scale)
+    dq, dk, dv = vsa.vsa_block_sparse_attn_bwd(q, k, v, o, do, lse, rpd, cid, blk, blk, 1, scale)
+    torch.cuda.synchronize()
+    for h in (0, 12_345, 40_000, H - 1):
+        qh, kh, vh, dh = (to_np(t[:, :, h:h + 1]) for t in (q, k, v, do))
+        o_ref, lse_ref = oracle.attention(qh, kh, vh, rp, ci, blk, blk, scale, 1)
+        _check(o[:, :, h:h + 1], lse[:, h:h + 1], o_ref, lse_ref, torch.bfloat16)
+        refs = oracle.attention_bwd(qh, kh, vh, dh, rp, ci, blk, blk, scale, 1)
+        for got, ref in zip((dq, dk, dv), refs):
+            err = np.abs(to_np(got[:, :, h:h + 1]) - ref)
+            assert err.max() <= BWD_BF16_MAX * np.abs(ref).max() and err.mean() <= BWD_BF16_MEAN * np.abs(ref).mean()
+
+
 def test_attention_deterministic_and_dense_mask():
     q, k, v = (rand((1, 1500, 2, 128), torch.bfloat16, s).to(DEV) for s in (20, 21, 22))
     rp, ci = vsa.all_ones_mask(-(-1500 // 128), -(-1500 // 128), DEV)
