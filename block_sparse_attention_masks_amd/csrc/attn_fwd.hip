@@ -712,10 +712,12 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_fwd_bf16_ker
 
 // V^T packing for the VT forward: v [batch, nk, heads, D] -> vt [batch, heads, ceil(nk / 64),
 // D, 64], keys past nk zero; tiled (TL), key p of the packed order is raster row
-// raster_row(p), so the copy is in tile-major order.  Workgroup = one (batch, 64-key tile), all
-// heads, so it streams whole token rows; thread = 8 keys x 8 head-dim columns of one head
-// (16-byte loads of 8 key rows, an 8 x 8 transpose in registers, 16-byte stores of 8 head-dim
-// rows), kPackThreads / D heads at a time.  One HBM read and one write of V.
+// raster_row(p), so the copy is in tile-major order.  Workgroup = one (batch, 64-key tile) and
+// every gridDim.y-th pair (D = 128) or quad (D = 64) of heads -- all heads, streaming whole token
+// rows, unless there are too few (batch, tile) workgroups to fill the chip; thread = 8 keys x 8
+// head-dim columns of one head (16-byte loads of 8 key rows, an 8 x 8 transpose in registers,
+// 16-byte stores of 8 head-dim rows), kPackThreads / D heads at a time.  One HBM read and one
+// write of V.
 constexpr int kPackThreads = 256;
 template <int D, bool TL>
 __global__ __launch_bounds__(kPackThreads) void vt_pack_kernel(const uint16_t* __restrict__ v,
@@ -737,7 +739,7 @@ __global__ __launch_bounds__(kPackThreads) void vt_pack_kernel(const uint16_t* _
     const int64_t key = key0 + j;
     row[j] = !TL ? key : (run8 ? row0 + j : (key < nk ? (int64_t)raster_row(tg, (int)key) : key));
   }
-  for (int h = hsub; h < heads; h += HP) {
+  for (int h = (int)blockIdx.y * HP + hsub; h < heads; h += HP * (int)gridDim.y) {
     u32x4 in[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
@@ -1044,7 +1046,11 @@ hipError_t launch_attn_fwd(const AttnArgs& a, void* workspace, size_t workspace_
     const int64_t ntile = (a.nk + kBN - 1) / kBN;
     auto pack = a.head_dim == 64 ? (a.tiled ? vt_pack_kernel<64, true> : vt_pack_kernel<64, false>)
                                  : (a.tiled ? vt_pack_kernel<128, true> : vt_pack_kernel<128, false>);
-    hipLaunchKernelGGL(pack, dim3((unsigned)(a.batch * ntile)), dim3(kPackThreads), 0, stream,
+    // heads split over gridDim.y until about 1,024 workgroups (1 when the tiles alone give that)
+    const int hp = kPackThreads / a.head_dim;
+    const int64_t hsplit = std::max<int64_t>(1, std::min<int64_t>((a.heads + hp - 1) / hp,
+                                                                  (1024 + a.batch * ntile - 1) / (a.batch * ntile)));
+    hipLaunchKernelGGL(pack, dim3((unsigned)(a.batch * ntile), (unsigned)hsplit), dim3(kPackThreads), 0, stream,
                        (const uint16_t*)a.v, vt, a.nk, a.heads, ntile, tg);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
