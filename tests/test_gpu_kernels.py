@@ -293,6 +293,54 @@ def test_attention_widest_token_rows():
             assert err.max() <= BWD_BF16_MAX * np.abs(ref).max() and err.mean() <= BWD_BF16_MEAN * np.abs(ref).mean()
 
 
+def test_forward_captured_in_hip_graph():
+    """Both forward entries (workspace argument; the library's fixed array) captured in a HIP graph
+    on a default-priority stream and replayed three times, with other device work and
+    synchronisations between replays and the inputs rewritten in place before the last one: each
+    replay equals the eager call on the same inputs bit for bit.  Given out, lse and the
+    workspace, neither call allocates, synchronises or records a memset, so the graph holds
+    kernel launches only (the grouped plan: union lists, V^T packing, attention)."""
+    B, H, D, nq, nk, bq, bk = 1, 8, 128, 2000, 2048, 64, 64
+    slabs, scale = B * H, D ** -0.5
+    q, k, v = (rand((B, n, H, D), torch.bfloat16, sd).to(DEV) for n, sd in ((nq, 110), (nk, 111), (nk, 112)))
+    q2 = rand((B, nq, H, D), torch.bfloat16, 113).to(DEV)
+    rng = np.random.default_rng(114)
+    keep = rng.random((slabs * -(-nq // bq), -(-nk // bk))) < 0.4
+    keep[:, 0] = True
+    rp, ci = oracle.csr_from_bool(keep)
+    rpd, cid = torch.from_numpy(rp).to(DEV), torch.from_numpy(ci).to(DEV)
+    ws = torch.empty(vsa.attn_fwd_workspace_bytes(q, k, rpd, cid, bq, bk, slabs), dtype=torch.uint8, device=DEV)
+
+    def eager():
+        o_w, l_w = vsa.vsa_block_sparse_attn_fwd(q, k, v, rpd, cid, bq, bk, slabs, scale, workspace=ws)
+        o_s, l_s = vsa.vsa_block_sparse_attn_fwd_static(q, k, v, rpd, cid, bq, bk, torch.empty_like(q),
+                                                        torch.empty((B, H, nq), dtype=torch.float32, device=DEV),
+                                                        slabs, scale)
+        torch.cuda.synchronize()
+        return o_w, l_w, o_s, l_s
+
+    ref = eager()          # also resolves the fixed array's address before any capture
+    outs = [torch.empty_like(q), torch.empty((B, H, nq), dtype=torch.float32, device=DEV),
+            torch.empty_like(q), torch.empty((B, H, nq), dtype=torch.float32, device=DEV)]
+    graph, side = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=side):
+        vsa.vsa_block_sparse_attn_fwd(q, k, v, rpd, cid, bq, bk, slabs, scale, out=outs[0], lse=outs[1],
+                                      workspace=ws)
+        vsa.vsa_block_sparse_attn_fwd_static(q, k, v, rpd, cid, bq, bk, outs[2], outs[3], slabs, scale)
+    for rep in range(3):
+        if rep == 2:
+            q.copy_(q2)
+            ref = eager()
+        x = torch.randn(1 << 22, device=DEV)
+        _ = (x * 2).sum().item()                       # other work and a synchronisation between replays
+        for t in outs:
+            t.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(outs, ref):
+            assert torch.equal(got, want), rep
+
+
 def test_attention_deterministic_and_dense_mask():
     q, k, v = (rand((1, 1500, 2, 128), torch.bfloat16, s).to(DEV) for s in (20, 21, 22))
     rp, ci = vsa.all_ones_mask(-(-1500 // 128), -(-1500 // 128), DEV)
