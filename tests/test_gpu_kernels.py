@@ -341,6 +341,39 @@ def test_forward_captured_in_hip_graph():
             assert torch.equal(got, want), rep
 
 
+def test_calls_on_two_streams_overlap_safely():
+    """The entries that take a workspace hold no state of their own: two different problems
+    run at the same time on two streams (default priority), forward then backward on each,
+    give the same bits as the same calls one after the other."""
+    probs = []
+    for sd, (H, nq, nk, bq, bk) in enumerate(((6, 2000, 2048, 64, 64), (3, 1500, 1300, 128, 128))):
+        q, k, v, do = (rand((1, n, H, 128), torch.bfloat16, 120 + 4 * sd + i).to(DEV)
+                       for i, n in enumerate((nq, nk, nk, nq)))
+        keep = np.random.default_rng(130 + sd).random((H * -(-nq // bq), -(-nk // bk))) < 0.5
+        keep[:, -1] = True
+        rp, ci = oracle.csr_from_bool(keep)
+        probs.append((q, k, v, do, torch.from_numpy(rp).to(DEV), torch.from_numpy(ci).to(DEV), bq, bk, H))
+
+    def run(p):
+        q, k, v, do, rp, ci, bq, bk, H = p
+        o, lse = vsa.vsa_block_sparse_attn_fwd(q, k, v, rp, ci, bq, bk, H, 128 ** -0.5)
+        return (o, lse) + vsa.vsa_block_sparse_attn_bwd(q, k, v, o, do, lse, rp, ci, bq, bk, H, 128 ** -0.5)
+
+    seq = [run(p) for p in probs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(2):
+        got = [None, None]
+        for i, (p, st) in enumerate(zip(probs, streams)):
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                got[i] = run(p)
+        torch.cuda.synchronize()
+        for a, b in zip(got, seq):
+            for x, y in zip(a, b):
+                assert torch.equal(x, y), rep
+
+
 def test_attention_deterministic_and_dense_mask():
     q, k, v = (rand((1, 1500, 2, 128), torch.bfloat16, s).to(DEV) for s in (20, 21, 22))
     rp, ci = vsa.all_ones_mask(-(-1500 // 128), -(-1500 // 128), DEV)
