@@ -650,26 +650,27 @@ def test_grouped_query_blocks(case):
 
 
 # ------------------------------------------------ groups across frames (radial)
-@pytest.mark.parametrize("T,S,block,H,per_head", [
-    (12, 1000, 128, 16, False),   # 7.8 blocks per frame: groups 7 blocks apart, a ragged last block
-    (9, 768, 64, 40, True),       # 12 blocks per frame, 64-row blocks (two tiles per stage), per-head masks
-    (40, 300, 128, 8, False),     # 2.3 blocks per frame: groups 2 apart
+@pytest.mark.parametrize("T,S,block,B,H,per_head", [
+    (12, 1000, 128, 1, 16, False),   # 7.8 blocks per frame: groups 7 blocks apart, a ragged last block
+    (9, 768, 64, 1, 40, True),       # 12 blocks per frame, 64-row blocks (two tiles per stage), per-head masks
+    (40, 300, 128, 1, 8, False),     # 2.3 blocks per frame: groups 2 apart
+    (12, 640, 128, 2, 8, True),      # two batches, a mask per (batch, head)
 ])
-def test_radial_grouping_across_frames(T, S, block, H, per_head):
+def test_radial_grouping_across_frames(T, S, block, B, H, per_head):
     """vsa_radial_attn_fwd groups query blocks at the same place of consecutive frames; it
     computes the same thing as the plain forward (bit for bit for 65- to 128-row blocks,
     whose rows walk the same tiles in the same order), with the radial mask or any other."""
     n = T * S
     nb = -(-n // block)
-    q, k, v = (rand((1, n, H, 128), torch.bfloat16, 95 + i) for i in range(3))
+    q, k, v = (rand((B, n, H, 128), torch.bfloat16, 95 + i) for i in range(3))
     if per_head:
         rng = np.random.default_rng(96)
-        keep = rng.random((H * nb, nb)) < 0.4
-        keep[np.arange(H * nb), rng.integers(0, nb, size=H * nb)] = True
+        keep = rng.random((B * H * nb, nb)) < 0.4
+        keep[np.arange(B * H * nb), rng.integers(0, nb, size=B * H * nb)] = True
         keep[1] = False
         rp_h, ci_h = oracle.csr_from_bool(keep)
         rp, ci = torch.from_numpy(rp_h).to(DEV), torch.from_numpy(ci_h).to(DEV)
-        slabs = H
+        slabs = B * H
     else:
         rp, ci = vsa.vsa_mask_radial(T, S, block, DEV)
         rp_h, ci_h = csr_np(rp, ci)
@@ -684,12 +685,12 @@ def test_radial_grouping_across_frames(T, S, block, H, per_head):
         assert (o_f.float() - o_p.float()).abs().max() <= BF16_MAX
     rng = np.random.default_rng(97)
     errs = []
-    for h in (0, H - 1):
+    for b, h in ((0, 0), (B - 1, H - 1)):
         rows = np.concatenate([rng.choice(n, 96, replace=False), [n - 1]])
-        base = 0 if slabs == 1 else h * nb
-        ref, _ = oracle.attention_rows(to_np(q[0, rows, h]), rows, to_np(k[0, :, h]), to_np(v[0, :, h]),
+        base = 0 if slabs == 1 else (b * H + h) * nb
+        ref, _ = oracle.attention_rows(to_np(q[b, rows, h]), rows, to_np(k[b, :, h]), to_np(v[b, :, h]),
                                        rp_h, ci_h, base, block, block, 128 ** -0.5)
-        errs.append(np.abs(o_f[0, rows, h].cpu().double().numpy() - ref))
+        errs.append(np.abs(o_f[b, rows, h].cpu().double().numpy() - ref))
     err = np.concatenate(errs)
     assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN
 
