@@ -572,6 +572,39 @@ def test_backward_large_heads_xcd_runs():
         assert mx <= BWD_BF16_MAX and mn <= BWD_BF16_MEAN, name
 
 
+@pytest.mark.parametrize("B,H,nq,nk,bq,bk,dens,per_head,dtype", [
+    (2, 3, 700, 900, 128, 128, 0.5, True, torch.bfloat16),     # a mask per (batch, head), ragged blocks
+    (2, 16, 1100, 2100, 64, 64, 0.4, True, torch.bfloat16),    # 544 key-block groups: grouped dK/dV
+    (2, 2, 500, 600, 64, 64, 0.5, False, torch.float32),       # one shared mask, fp32 path
+])
+def test_attention_backward_two_batches(B, H, nq, nk, bq, bk, dens, per_head, dtype):
+    """The backward with two batches against the oracle on every element."""
+    D = 128
+    scale = D ** -0.5
+    q, k, v, do = (rand((B, n, H, D), dtype, 140 + i) for i, n in enumerate((nq, nk, nk, nq)))
+    slabs = B * H if per_head else 1
+    nbq, nbk = -(-nq // bq), -(-nk // bk)
+    rng = np.random.default_rng(145)
+    keep = rng.random((slabs * nbq, nbk)) < dens
+    keep[np.arange(slabs * nbq), rng.integers(0, nbk, size=slabs * nbq)] = True
+    rp, ci = oracle.csr_from_bool(keep)
+    rpd, cid = torch.from_numpy(rp).to(DEV), torch.from_numpy(ci).to(DEV)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = vsa.vsa_block_sparse_attn_fwd(qd, kd, vd, rpd, cid, bq, bk, slabs, scale)
+    dq, dk, dv = vsa.vsa_block_sparse_attn_bwd(qd, kd, vd, o, dod, lse, rpd, cid, bq, bk, slabs, scale)
+    refs = oracle.attention_bwd(to_np(q), to_np(k), to_np(v), to_np(do), rp, ci, bq, bk, scale, slabs)
+    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
+        err = np.abs(got.cpu().double().numpy() - ref)
+        mx, mn = err.max() / np.abs(ref).max(), err.mean() / np.abs(ref).mean()
+        print(f"two-batch bwd {B}x{H} {name}: max_norm {mx:.2e} mean_norm {mn:.2e}", flush=True)
+        if dtype == torch.float32:
+            assert mx <= BWD_F32_MAX, name
+        else:
+            assert mx <= BWD_BF16_MAX and mn <= BWD_BF16_MEAN, name
+        for b in range(B):   # both batches carry gradient (nothing left at zero by an indexing slip)
+            assert np.abs(got[b].cpu().double().numpy()).max() > 0, (name, b)
+
+
 # ------------------------------------------------- grouped small query blocks
 GROUPED_CASES = [
     # batch, heads, D, nq, nk, bq, bk, density, per-head masks
