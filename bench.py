@@ -644,7 +644,7 @@ def main():
     med, mn = time_hbm_pass(lambda: path.vsa.vsa_block_sics(path.ka, path.bk, out=sics_out), stream, flush)
     sics = hbm(med, mn, k_bytes, kernel="sics_kernel", tensor="K in attention order", block=path.bk,
                ratio_to_attn=round(med / attn_ms, 5))
-    pool_out = torch.empty((path.B, path.H, path.nbk, path.D), dtype=torch.float64, device=dev)
+    pool_out = torch.empty((path.B, path.nbk, path.H, path.D), dtype=torch.float64, device=dev)
     med, mn = time_hbm_pass(lambda: path.vsa.vsa_block_mean_pool(path.ka, path.bk, out=pool_out), stream, flush)
     pool = hbm(med, mn, k_bytes, kernel="pool_kernel<true>",
                tensor="K in attention order", block=path.bk,

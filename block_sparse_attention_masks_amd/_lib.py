@@ -211,17 +211,17 @@ def vsa_mask_union(rp_a, ci_a, slabs_a, rp_b, ci_b, slabs_b, n_qblocks, n_kblock
 
 def vsa_block_mean_pool(x, block, out=None):
     """Mean of each block's valid token rows of x [B, N, heads, head_dim] (bf16 or fp32)
-    -> fp64 [B, heads, ceil(N / block), head_dim]."""
+    -> fp64 [B, ceil(N / block), heads, head_dim] (block-major, like x)."""
     _require(x, "x")
     if x.dtype not in _DTYPE:
         raise ValueError("x must be bfloat16 or float32")
     B, N, H, D = x.shape
     nb = -(-N // block)
     if out is None:
-        out = torch.empty((B, H, nb, D), dtype=torch.float64, device=x.device)
+        out = torch.empty((B, nb, H, D), dtype=torch.float64, device=x.device)
     _require(out, "out", x.device)
-    if out.dtype != torch.float64 or tuple(out.shape) != (B, H, nb, D):
-        raise ValueError("out must be float64 [B, heads, n_blocks, head_dim]")
+    if out.dtype != torch.float64 or tuple(out.shape) != (B, nb, H, D):
+        raise ValueError("out must be float64 [B, n_blocks, heads, head_dim]")
     _check(lib().vsa_block_mean_pool(_ptr(x), _DTYPE[x.dtype], B, H, D, N, block, _ptr(out), _stream(x)),
            "vsa_block_mean_pool")
     return out

@@ -238,13 +238,14 @@ vsa_status vsa_mask_remap(const int32_t* row_ptr, const int32_t* col_idx, int64_
  *
  * NABLA explainer (aibr.jp/archives/124678), sec. 3: Q and K are average-pooled per
  * block before the small attention map is formed.  This is that pooling step on one
- * tensor (vsa_mask_nabla runs the same kernel on Q and K): out[b, h, i, :] = the mean
- * over the valid tokens t of block i (the last block may be ragged) of x[b, t, h, :].
+ * tensor (vsa_mask_nabla runs the same kernel on Q and K): out[b, i, h, :] = the mean
+ * over the valid tokens t of block i (the last block may be ragged) of x[b, t, h, :]
+ * (block-major, the order of the token tensor itself).
  * The sums are accumulated in fp64 (exact for bf16 rows) and divided once by the
  * block's token count.
  *
  * x     device, [batch, n, heads, head_dim], dtype VSA_BF16 or VSA_F32, 16-byte aligned.
- * out   device, [batch, heads, ceil(n / block), head_dim] doubles, 8-byte aligned.
+ * out   device, [batch, ceil(n / block), heads, head_dim] doubles, 8-byte aligned.
  * Errors: VSA_ERR_NULL, VSA_ERR_DTYPE, VSA_ERR_SHAPE (non-positive sizes, batch above
  * 65535, ceil(n / block) * ceil(heads * head_dim / 512) above 2^31 - 1),
  * VSA_ERR_UNSUPPORTED (head_dim not 64/128, alignment), VSA_ERR_HIP.

@@ -116,6 +116,19 @@ def test_mask_nabla_bit_exact(nq, nk, bq, bk, thr, dtype):
     print(f"nabla mask {nq}x{nk} blocks {bq}/{bk} thr {thr}: {check_nabla(rp, ci, to_np(q), to_np(k), bq, bk, scale, thr)}")
 
 
+def test_mask_nabla_two_batches_bit_exact():
+    """Two batches of five heads, ragged last blocks on both sides: the pooled means of every
+    (batch, block, head) reach the score of their own (batch, head) slab."""
+    q = rand((2, 600, 5, 128), torch.bfloat16, 12, 1.0)
+    k = rand((2, 1000, 5, 128), torch.bfloat16, 13, 1.0)
+    q[..., :8] += 2.0 * torch.linspace(-1, 1, 600).reshape(1, 600, 1, 1).to(q.dtype)
+    k[..., :8] += 2.0 * torch.linspace(-1, 1, 1000).reshape(1, 1000, 1, 1).to(k.dtype)
+    q[1] *= -1.0   # the second batch keeps other blocks than the first
+    scale = 128 ** -0.5
+    rp, ci = csr_np(*vsa.vsa_mask_nabla(q.to(DEV), k.to(DEV), 64, 64, scale, threshold=0.8))
+    print(f"nabla mask 2 batches: {check_nabla(rp, ci, to_np(q), to_np(k), 64, 64, scale, 0.8)}")
+
+
 @pytest.mark.parametrize("nk,bk,forced,topk", [
     (3000, 64, [(0, 5), (40, 47)], 6),
     (2000, 1, [(0, 25), (1900, 2000)], 16),     # 2,000 key blocks: 8 sort slots per thread
@@ -418,7 +431,9 @@ def test_block_mean_pool_bit_exact(B, N, H, D, block, dtype):
     x = rand((B, N, H, D), dtype, 33)
     got = vsa.vsa_block_mean_pool(x.to(DEV), block).cpu().numpy()
     xn = x.double().numpy()
-    want = np.stack([np.stack([oracle.pool_blocks(xn[b, :, h], block) for h in range(H)]) for b in range(B)])
+    # the library writes the means block-major, [B, blocks, heads, D]
+    want = np.stack([np.stack([oracle.pool_blocks(xn[b, :, h], block) for h in range(H)], axis=1)
+                     for b in range(B)])
     assert got.shape == want.shape and np.array_equal(got, want)
 
 
