@@ -91,7 +91,7 @@ struct NablaArgs {
 };
 size_t nabla_workspace_bytes(int64_t batch, int heads, int head_dim, int64_t nq, int64_t nk,
                              int block_q, int block_k);
-// Mean of the valid rows of each block: x [batch, n, heads, D] -> out [batch, heads, nb, D] fp64
+// Mean of the valid rows of each block: x [batch, n, heads, D] -> out [batch, nb, heads, D] fp64
 // (the pooling pass of the NABLA mask on one tensor).
 hipError_t launch_block_pool(const void* x, int bf16, int64_t batch, int heads, int D, int64_t n, int block,
                              double* out, hipStream_t stream);
