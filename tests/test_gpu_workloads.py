@@ -372,3 +372,50 @@ def test_backward_sta_workload():
         # measured), so the mean bound is 4 * 2^-9.
         assert mx <= 8 * 2.0 ** -9 and mn <= 4 * 2.0 ** -9, name
     log(f"sta bwd: done {time.time() - t0:.1f}s")
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_backward_radial_workload():
+    """dq at the radial workload's full size, as the bench times it (the shared radial mask,
+    the frame-grouped forward, then the backward in its XCD-run work order): 4 heads x 64
+    sampled query rows, the ragged last token among them, each against the oracle's own
+    evaluation of that row.  dk and dv are not sampled here: an oracle key block of this mask
+    needs the full softmax of the ~100,000 query rows that keep it (a teraflop in fp64); the
+    270,000-key test in test_gpu_kernels covers those kernels in the same work order."""
+    cfg = CONFIGS["radial"]
+    T, Hg, Wg = cfg["grid"]
+    S, blk, H, D = Hg * Wg, cfg["block"], cfg["heads"], cfg["head_dim"]
+    scale = D ** -0.5
+    t0 = time.time()
+    x = gen.make_inputs("radial")
+    qd, kd, vd = (x[w].to(DEV) for w in ("q", "k", "v"))
+    gd = torch.Generator(device=DEV).manual_seed(79)
+    dd = torch.randn(qd.shape, generator=gd, device=DEV).to(torch.bfloat16)
+    rp_d, ci_d = vsa.vsa_mask_radial(T, S, blk, DEV)
+    o, lse = vsa.vsa_radial_attn_fwd(qd, kd, vd, rp_d, ci_d, blk, S)
+    dq, dk, dv = vsa.vsa_block_sparse_attn_bwd(qd, kd, vd, o, dd, lse, rp_d, ci_d, blk, blk, 1, scale)
+    torch.cuda.synchronize()
+    del dk, dv
+    rp, ci = csr_np(rp_d, ci_d)
+    orp, oci = oracle.mask_radial(T, S, blk)
+    assert np.array_equal(rp, orp) and np.array_equal(ci, oci)
+    log(f"radial bwd: GPU done {time.time() - t0:.1f}s")
+    rng = np.random.default_rng(80)
+    nq = qd.shape[1]
+    errs, refs = [], []
+    for h in rng.choice(H, 4, replace=False):
+        rows = np.sort(rng.choice(nq - 1, 63, replace=False))
+        rows = np.append(rows, nq - 1)                        # the ragged last block's last row
+        qh, kh, vh = (x[w][0, :, h].double().numpy() for w in ("q", "k", "v"))
+        dh = dd[0, rows, h].cpu().double().numpy()
+        ref = oracle.attention_bwd_query_rows(qh[rows], rows, dh, kh, vh, orp, oci, 0, blk, blk, scale)
+        errs.append(np.abs(dq[0, rows, h].cpu().double().numpy() - ref))
+        refs.append(np.abs(ref))
+    e, r = np.concatenate(errs), np.concatenate(refs)
+    mx, mn = e.max() / r.max(), e.mean() / r.mean()
+    log(f"radial bwd dq: max_norm {mx:.2e} mean_norm {mn:.2e} ({time.time() - t0:.1f}s)")
+    # the bounds of the sta workload's backward, for the same reason: D built from the
+    # forward's bf16 O enters dS while dq is a difference of near-equal terms under the
+    # positional code's peaked attention
+    assert mx <= 8 * 2.0 ** -9 and mn <= 4 * 2.0 ** -9
