@@ -120,12 +120,26 @@ def test_radial_token_bruteforce(T, S, block):
     assert np.array_equal(oracle.csr_to_bool(rp, ci, len(rp) - 1), radial_bruteforce(T, S, block))
 
 
-def test_radial_token_rule_matches_bruteforce_rule():
-    T, S = 9, 11
+@pytest.mark.parametrize("T,S", [(9, 11), (9, 8), (17, 16)])
+def test_radial_token_rule_matches_bruteforce_rule(T, S):
+    # frame sizes divisible by 2^r reach the boundary |ds| * 2^r = S, which drops the pair
     n = np.arange(T * S)
     keep = oracle.radial_keep_tokens(n[:, None] // S, n[:, None] % S, n[None] // S, n[None] % S, S)
     blocks = radial_bruteforce(T, S, 1)
     assert np.array_equal(keep, blocks)
+
+
+def test_radial_token_rule_boundary_pairs():
+    """Hand-worked pairs at the edge of the window, S = 8 (frame, in-frame index):
+    d = 2, 3 (r = 1) keep |ds| <= 3; d = 4..7 (r = 2) keep |ds| <= 1; d = 8 (r = 3) keeps
+    ds = 0 only; d <= 1 keeps everything."""
+    S = 8
+    cases = [((0, 0), (1, 7), True), ((0, 0), (2, 3), True), ((0, 0), (2, 4), False),
+             ((0, 0), (3, 3), True), ((0, 0), (3, 4), False), ((0, 0), (4, 1), True),
+             ((0, 0), (4, 2), False), ((0, 7), (7, 6), True), ((0, 7), (7, 5), False),
+             ((0, 3), (8, 3), True), ((0, 3), (8, 4), False), ((5, 2), (1, 3), True)]
+    for (fq, sq), (fk, sk), want in cases:
+        assert bool(oracle.radial_keep_tokens(fq, sq, fk, sk, S)) == want, (fq, sq, fk, sk)
 
 
 def test_radial_near_frames_dense_and_single_frame():
