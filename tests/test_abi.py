@@ -318,3 +318,43 @@ def test_bwd_validation(L):
     assert bwd(L, dq=ODD)[0] == E_UNSUP
     assert bwd(L, H=65536, query=True)[0] == E_UNSUP                 # bf16 rows of 2^24 bytes
     assert bwd(L, H=65535, query=True)[0] == OK
+
+
+C_CALLER = r"""
+#include "vsa.h"
+#include <stdio.h>
+/* a C caller: the header parses as C and the library links; no call here reaches a kernel */
+int main(void) {
+  printf("%s\n", vsa_status_string(VSA_ERR_SHAPE));
+  if (vsa_mask_radial(0, 0, 0, 0, 0, 0, 0) != VSA_ERR_NULL) return 1;
+  size_t need = 0;
+  vsa_select sel = {0.9, 0, 0, 0};
+  (void)sel;
+  if (vsa_block_sparse_attn_fwd(0, 0, 0, 0, 0, VSA_BF16, 1, 1, 128, 1, 1, 64, 64, 0, 0, 1, 1.0f, 0, &need, 0) !=
+      VSA_ERR_NULL)
+    return 2;
+  return 0;
+}
+"""
+
+
+@pytest.mark.parametrize("compiler,std", [("gcc", "-std=c99"), ("g++", "-std=c++17")])
+def test_header_compiles_and_links_from_c(L, tmp_path, compiler, std):
+    """include/vsa.h as a C (and C++) caller sees it: it compiles warning-free, the program links
+    against libvsa.so by the declared names, and the calls return the documented codes."""
+    import shutil
+    import subprocess
+    if shutil.which(compiler) is None:
+        pytest.skip(f"{compiler} not available")
+    src = tmp_path / ("caller.c" if compiler == "gcc" else "caller.cpp")
+    src.write_text(C_CALLER)
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    cmd = [compiler, std, "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+           "-I", "/opt/rocm/include", str(src), "-o", str(exe), "-L", libdir, f"-l:{os.path.basename(_lib.LIB_PATH)}",
+           f"-Wl,-rpath,{libdir}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert r.stdout.strip() == _lib.status_string(E_SHAPE)
